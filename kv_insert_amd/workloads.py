@@ -1,0 +1,180 @@
+"""Seeded synthetic inputs of the decode-batch front's workloads.
+
+This module only draws inputs: it holds none of the front's arithmetic and
+imports neither the library nor any checker, so the HIP path and the CPU
+oracle can both be fed from it.
+
+Shapes and distributions (qkv_front page, module summary, for 1 <= M <= 16;
+cute_ops page, split_qkv and the attn2 contract for widths and the cache):
+  x         bf16 [M, 8192] ~ N(0, 1), optionally with outlier rows x30;
+  W         bf16 [N, 8192] ~ N(0, 0.011^2), N = 1152 * nkv;
+  positions int64 [M], slots int64 [M] (distinct), per workload;
+  cos_sin   fp32 [rows, 64]: row p holds cos(p * f_i) in column i and
+            sin(p * f_i) in column 32 + i, f_i = theta^(-2i/64), theta 10000
+            (the interleaved rotary table's usual construction);
+  kv_cache  bf16 [pages, nkv, 16, 128] prefilled with random bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+HIDDEN = 8192
+HEAD_DIM = 64
+QHEADS_PER_KV = 8
+PAGE_SLOTS = 16
+SLOT_WIDTH = 128
+EPS = 1e-6
+ROPE_THETA = 10000.0
+W_STD = 0.011
+
+
+def n_cols(nkv: int) -> int:
+    return 2 * (QHEADS_PER_KV * nkv + nkv) * HEAD_DIM
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    nkv: int
+    pages: int
+    table_rows: int
+    pos_mode: str          # "uniform" | "consecutive"
+    pos_lo: int
+    pos_hi: int            # exclusive
+    slot_mode: str         # "uniform" (one token) | "consecutive" | "distinct"
+    slot_hi: int           # exclusive bound for the first / random slots
+    wsets: int             # weight sets rotated per call
+    outlier_p: float = 0.0  # probability that an x row is scaled x30
+    force_outlier: bool = False
+    index: int = 0
+
+    @property
+    def N(self) -> int:
+        return n_cols(self.nkv)
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the front must move once per call: W, x, y, the cos|sin
+        rows, positions + slots, and the K|V slots written."""
+        M, N = self.M, self.N
+        return (2 * N * HIDDEN + 2 * M * HIDDEN + 2 * M * N + 4 * HEAD_DIM * M
+                + 16 * M + 2 * SLOT_WIDTH * M * self.nkv)
+
+
+# The five workloads the front is measured and checked on.
+C1 = Workload("m1_nkv1_n1152", M=1, nkv=1, pages=64, table_rows=4096,
+              pos_mode="uniform", pos_lo=0, pos_hi=4096,
+              slot_mode="uniform", slot_hi=1024, wsets=1, index=1)
+C2 = Workload("m8_nkv2_n2304_draft", M=8, nkv=2, pages=512, table_rows=4104,
+              pos_mode="consecutive", pos_lo=8, pos_hi=4096,
+              slot_mode="consecutive", slot_hi=512 * 16 - 7, wsets=1, index=2)
+C3 = Workload("m8_nkv8_n9216", M=8, nkv=8, pages=8192, table_rows=131072,
+              pos_mode="uniform", pos_lo=0, pos_hi=131072,
+              slot_mode="distinct", slot_hi=8192 * 16, wsets=4, index=3)
+C4 = Workload("m16_nkv8_n9216_outliers", M=16, nkv=8, pages=16384,
+              table_rows=32768, pos_mode="uniform", pos_lo=0, pos_hi=32768,
+              slot_mode="distinct", slot_hi=16384 * 16, wsets=4,
+              outlier_p=0.01, force_outlier=True, index=4)
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4)}
+
+SWEEP_M = (1, 2, 3, 4, 5, 8, 12, 16)
+SWEEP_NKV = (1, 2, 4, 8)
+
+
+def sweep(M: int, nkv: int, wsets: int = 32) -> Workload:
+    """One point of the M x KV-heads sweep: cache of 64K slots, positions
+    uniform in [0, 131072), random distinct slots."""
+    return Workload(f"sweep_m{M}_nkv{nkv}", M=M, nkv=nkv, pages=4096,
+                    table_rows=131072, pos_mode="uniform", pos_lo=0,
+                    pos_hi=131072, slot_mode="distinct", slot_hi=4096 * 16,
+                    wsets=wsets, index=5)
+
+
+def seed_of(w: Workload, set_index: int) -> int:
+    return 1000 * w.index + set_index
+
+
+def rope_table(rows: int, theta: float = ROPE_THETA) -> torch.Tensor:
+    """fp32 [rows, 64]: 32 cos | 32 sin, built in float64, stored as fp32."""
+    pos = torch.arange(rows, dtype=torch.float64)[:, None]
+    i = torch.arange(HEAD_DIM // 2, dtype=torch.float64)[None, :]
+    ang = pos * torch.pow(torch.tensor(theta, dtype=torch.float64), -2.0 * i / HEAD_DIM)
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32).contiguous()
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def make_weights(w: Workload, set_index: int = 0, device="cpu") -> torch.Tensor:
+    """bf16 [N, 8192] ~ N(0, 0.011^2), drawn on the CPU (reproducible)."""
+    g = _gen(seed_of(w, set_index) * 7919 + 1)
+    W = torch.randn(w.N, HIDDEN, generator=g, dtype=torch.float32) * W_STD
+    return W.to(torch.bfloat16).to(device)
+
+
+def make_weights_on_device(w: Workload, set_index: int, device) -> torch.Tensor:
+    """Same distribution drawn by the device's own generator (fast, for
+    large rotated weight pools that are never checked element by element)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(w, set_index) * 7919 + 2)
+    W = torch.empty(w.N, HIDDEN, dtype=torch.bfloat16, device=device)
+    W.normal_(0.0, W_STD, generator=g)
+    return W
+
+
+def make_tokens(w: Workload, set_index: int = 0, device="cpu", M: int | None = None):
+    """x, positions, slots for one call."""
+    M = w.M if M is None else M
+    g = _gen(seed_of(w, set_index) * 7919 + 3)
+    x = torch.randn(M, HIDDEN, generator=g, dtype=torch.float32)
+    if w.outlier_p > 0:
+        hit = torch.rand(M, generator=g) < w.outlier_p
+        if w.force_outlier:
+            hit[int(torch.randint(0, M, (1,), generator=g))] = True
+        x[hit] *= 30.0
+    x = x.to(torch.bfloat16)
+    if w.pos_mode == "consecutive":
+        p0 = int(torch.randint(w.pos_lo, w.pos_hi, (1,), generator=g))
+        positions = torch.arange(p0, p0 + M, dtype=torch.int64)
+    else:
+        positions = torch.randint(w.pos_lo, w.pos_hi, (M,), generator=g, dtype=torch.int64)
+    if w.slot_mode == "consecutive":
+        s0 = int(torch.randint(0, w.slot_hi, (1,), generator=g))
+        slots = torch.arange(s0, s0 + M, dtype=torch.int64)
+    elif w.slot_mode == "uniform":
+        slots = torch.randint(0, w.slot_hi, (M,), generator=g, dtype=torch.int64)
+    else:
+        slots = torch.randperm(w.slot_hi, generator=g)[:M].to(torch.int64)
+    assert int(positions.max()) < w.table_rows
+    assert int(slots.max()) < w.pages * PAGE_SLOTS
+    return x.to(device), positions.to(device), slots.to(device)
+
+
+def make_cache(w: Workload, device="cpu", seed: int | None = None) -> torch.Tensor:
+    """bf16 [pages, nkv, 16, 128] filled with random bit patterns."""
+    g = _gen((seed_of(w, 0) if seed is None else seed) * 7919 + 4)
+    n = w.pages * w.nkv * PAGE_SLOTS * SLOT_WIDTH
+    bits = torch.randint(-32768, 32768, (n,), generator=g, dtype=torch.int32).to(torch.int16)
+    return bits.view(torch.bfloat16).reshape(w.pages, w.nkv, PAGE_SLOTS, SLOT_WIDTH).to(device)
+
+
+def bits(t: torch.Tensor):
+    """numpy uint16 view of a bf16 tensor's bit patterns (CPU copy)."""
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def describe(w: Workload) -> dict:
+    return {"workload": w.name, "M": w.M, "num_kv_heads": w.nkv, "N": w.N,
+            "K": HIDDEN, "weight_sets": w.wsets, "cache_pages": w.pages,
+            "table_rows": w.table_rows}
+
+
+def rope_angle(pos: int, pair: int, theta: float = ROPE_THETA) -> float:
+    """The rotation angle the table above encodes for (position, pair)."""
+    return pos * math.pow(theta, -2.0 * pair / HEAD_DIM)
