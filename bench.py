@@ -1,0 +1,170 @@
+"""Benchmark of the decode-batch attention front on one MI355X.
+
+One step is one qkvf_run call: the projection, norm, rotation, y store and
+K|V insert of M tokens, on weight set (step mod S) of S rotated sets so the
+weights come from HBM rather than the 256 MB MALL.  Prints ONE JSON line.
+
+Default workload: M = 8 tokens, 8 KV heads, N = 9216 (151 MB of bf16
+weights per set, 4 sets).  `value` is achieved GB/s of algorithmic bytes
+(W + x + y + cos|sin rows + indices + K|V slots) per call, inputs resident
+in HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import kv_insert_amd as qf  # noqa: E402
+from kv_insert_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default=wl.C3.name,
+                    help="one of " + ", ".join(wl.WORKLOADS) + " or sweep_m<M>_nkv<K>")
+    ap.add_argument("--wsets", type=int, default=0, help="override rotated weight sets")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--repeats", type=int, default=3, help="timed repeats; the median is kept")
+    return ap.parse_args()
+
+
+def workload_by_name(name: str) -> wl.Workload:
+    if name in wl.WORKLOADS:
+        return wl.WORKLOADS[name]
+    if name.startswith("sweep_m"):
+        m, k = name[len("sweep_m"):].split("_nkv")
+        return wl.sweep(int(m), int(k))
+    raise SystemExit(f"unknown workload {name}")
+
+
+class Pool:
+    """Device-resident inputs of S calls, rotated per step."""
+
+    def __init__(self, w: wl.Workload, sets: int):
+        dev = "cuda"
+        self.w = w
+        self.sets = sets
+        self.W = [wl.make_weights_on_device(w, s, dev) for s in range(sets)]
+        toks = [wl.make_tokens(w, s) for s in range(sets)]
+        self.x = [t[0].to(dev) for t in toks]
+        self.pos = [t[1].to(dev) for t in toks]
+        self.slots = [t[2].to(dev) for t in toks]
+        self.cos_sin = wl.rope_table(w.table_rows).to(dev)
+        self.cache = wl.make_cache(w).to(dev)
+        self.y = [torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+
+    def call(self, i: int, stream) -> None:
+        s = i % self.sets
+        qf.run(self.x[s], self.W[s], self.pos[s], self.slots[s], self.cos_sin, self.y[s],
+               self.cache, M=self.w.M, stream=stream)
+
+
+def cpu_baseline(w: wl.Workload, budget_s: float) -> dict | None:
+    """The oracle, as it stands, on full calls of the same workload (set 0),
+    timed on this host's cores; as many calls as fit the budget (>= 1)."""
+    if budget_s <= 0:
+        return None
+    import numpy as np
+
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    x, pos, slots = wl.make_tokens(w, 0)
+    W = wl.bits(wl.make_weights(w, 0))
+    xb = wl.bits(x)
+    table = wl.rope_table(w.table_rows).numpy()
+    cache = np.zeros((w.pages, w.nkv, wl.PAGE_SLOTS, wl.SLOT_WIDTH), np.uint16)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.front(xb, W, pos.numpy(), slots.numpy(), table, w.nkv, wl.EPS, cache,
+                     nthreads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (el / calls) * (calls + 1) > 2 * budget_s:
+            break
+    per_call = el / calls
+    return {"value": round(w.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
+            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "kind": "oracle",
+            "sample": f"{calls} full oracle calls of {w.name} (weight set 0), {threads} OpenMP threads"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {a.gpus}); the front is a "
+              "single-GPU kernel (sharding by KV heads is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    w = workload_by_name(a.workload)
+    sets = a.wsets or w.wsets
+    if sets < 2 and w.N * wl.HIDDEN * 2 * sets < 300e6:
+        # a single small weight set would sit in the 256 MB MALL: rotate
+        # enough sets to exceed it
+        sets = max(sets, int(600e6 // (w.N * wl.HIDDEN * 2)) + 1)
+    torch.cuda.set_device(0)
+    pool = Pool(w, sets)
+    qf.prepare(w.N, w.nkv, w.M)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(a.warmup):
+            pool.call(i, stream)
+    torch.cuda.synchronize()
+
+    times = []
+    for rep in range(a.repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(a.steps):
+            pool.call(a.warmup + i, stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / a.steps)  # ms per call
+    ms = sorted(times)[len(times) // 2]
+    nbytes = w.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    base = cpu_baseline(w, a.cpu_baseline_seconds)
+    out = {
+        "metric": "QKV-front achieved HBM GB/s (algorithmic bytes per call / time per call)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(wl.describe(w), weight_sets_rotated=sets,
+                       algorithmic_bytes_per_call=nbytes),
+        "roofline": {"bound": "hbm", "kernel": "front (projection + epilogue, whole call)",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": base,
+        "repeats_ms": [round(t, 6) for t in times],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

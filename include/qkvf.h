@@ -1,0 +1,140 @@
+/*
+ * libqkvfront: the decode-batch attention front on MI355X (gfx950).
+ *
+ * For 1 <= M <= 16 tokens one call computes, in the order below, what the
+ * QKV + o-gate projection followed by the unfused "q/k norm + rope + kv
+ * insert" op computes for a bf16 KV cache (qkv_front page, module summary;
+ * cute_ops page, qkv_front):
+ *   1. p = bf16(x @ W^T): x bf16 [M][8192], W bf16 [N][8192], fp32
+ *      accumulation, round to nearest even;
+ *   2. on each q and k head (64 columns) of each token: a weightless RMS
+ *      norm, n = p / sqrt(mean(p^2) + 1e-6), then the interleaved rotary
+ *      embedding of pairs (2i, 2i+1) by the cos|sin row of the token's
+ *      position; v and gate columns stay p;
+ *   3. the store of the result row y[m] = [q | k | v | gate] (cute_ops page,
+ *      split_qkv: per KV head 8 q heads, one k, one v and 8 gate heads, 64
+ *      columns each, so N = 1152 * num_kv_heads);
+ *   4. the insert of each token's k and v heads into its slot of the paged
+ *      cache [pages][num_kv_heads][16][128] bf16, K in elements 0..63 and V
+ *      in 64..127 of the slot (cute_ops page, attn2 contract).
+ * The result depends only on the launch shape, which is a function of
+ * (N, M) alone (qkv_front page, "Structure"): repeated calls are bitwise
+ * identical.
+ *
+ * All pointers are device pointers on the current HIP device.  The caller
+ * owns every tensor; the library owns only a small fp32 workspace per device
+ * (allocated by qkvf_prepare, freed by qkvf_release).  Functions return 0 or
+ * a qkvf_status code, never throw and never abort.
+ */
+#ifndef QKVF_H
+#define QKVF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (the reasons a call is refused: qkv_front page, function
+ * "unsupported"; cute_ops page, supports_call and unsupported_projection). */
+typedef enum {
+    QKVF_OK = 0,
+    QKVF_ERR_DEVICE = 1,        /* no current device, or it is not gfx950 */
+    QKVF_ERR_SHAPE = 2,         /* num_kv_heads not in {1,2,4,8} or N != 1152*num_kv_heads */
+    QKVF_ERR_ROWS = 3,          /* M outside [1, 16] */
+    QKVF_ERR_ALIGN = 4,         /* a pointer is not aligned as stated below */
+    QKVF_ERR_NULLPTR = 5,       /* a required pointer is NULL */
+    QKVF_ERR_NOT_PREPARED = 6,  /* no shape bound on this thread, or (N, M) not prepared on this device */
+    QKVF_ERR_ALLOC = 7,         /* workspace allocation failed */
+    QKVF_ERR_HIP = 8,           /* a HIP runtime call or a launch failed */
+    QKVF_ERR_RANGE = 9,         /* qkvf_check: a position or slot out of range, duplicate slots */
+    QKVF_ERR_OVERLAP = 10,      /* qkvf_check: an output overlaps another operand */
+    QKVF_ERR_MEMORY = 11        /* qkvf_check: a pointer is not device memory of the current device */
+} qkvf_status;
+
+/*
+ * Prepare the front for N output columns, num_kv_heads KV heads and every
+ * row count 1..M on the current device (qkv_front page, function "prepare":
+ * ready the variants before graph capture).  Validates the shape, checks the
+ * device is gfx950, allocates the device workspace once (2.25 MiB, the same
+ * for every shape), and binds (N, num_kv_heads) as the calling thread's
+ * current shape, which qkvf_run uses.  Call it again to switch shape; it is
+ * cheap after the first call.  Not to be called during graph capture.
+ * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS, QKVF_ERR_DEVICE, QKVF_ERR_ALLOC.
+ */
+int qkvf_prepare(int N, int num_kv_heads, int M);
+
+/*
+ * Enqueue one front call of M tokens on `stream` for the thread's current
+ * shape (qkv_front page, function "launch": the call without the full
+ * checks).
+ *   x          bf16 [M][8192], row-major, 16-byte aligned (read);
+ *   W          bf16 [N][8192], row-major, 16-byte aligned (read);
+ *   positions  int64 [M]: row of cos_sin for each token (read);
+ *   slots      int64 [M]: cache slot of each token, page = slot / 16,
+ *              offset = slot % 16; a negative slot writes no cache entry
+ *              (read);
+ *   cos_sin    fp32 [rows][64], row p = 32 cos | 32 sin of position p, or
+ *              NULL for a layer without RoPE (q and k are then only normed),
+ *              16-byte aligned (read);
+ *   y          bf16 [M][N], row-major, 16-byte aligned (written; rows >= M
+ *              are not touched);
+ *   kv_cache   bf16 [pages][num_kv_heads][16][128], 16-byte aligned (only
+ *              the M slots named by `slots` are written).
+ * The caller guarantees positions < rows of cos_sin, slots < pages * 16,
+ * distinct non-negative slots, and no overlap between y, kv_cache and the
+ * inputs (qkvf_check verifies all of these).  The call allocates nothing,
+ * never synchronizes and only enqueues work on `stream` (so it can be
+ * captured in a HIP graph).  Calls on one device share its workspace: they
+ * must be ordered (one stream, or streams ordered by events).
+ * Errors (cheap scalar checks only): QKVF_ERR_NOT_PREPARED, QKVF_ERR_ROWS,
+ * QKVF_ERR_NULLPTR, QKVF_ERR_ALIGN, QKVF_ERR_DEVICE, QKVF_ERR_HIP.
+ */
+int qkvf_run(const void *x, const void *W, const int64_t *positions,
+             const int64_t *slots, const float *cos_sin, void *y,
+             void *kv_cache, int M, hipStream_t stream);
+
+/*
+ * Full check of a call before it is launched (qkv_front page, function
+ * "unsupported"; cute_ops page, supports_call): shape, rows, alignment,
+ * that every pointer is device memory of the current device, that y and
+ * kv_cache overlap neither each other nor any input, and, when
+ * read_indices != 0, that every position is in [0, table_rows) and every
+ * slot is negative or in [0, pages * 16) with no slot repeated.
+ * read_indices copies positions and slots to the host and so synchronizes
+ * the device; with read_indices == 0 nothing is read from the device.
+ * Returns QKVF_OK or the first reason found.  It launches nothing.
+ */
+int qkvf_check(int N, int num_kv_heads, int M, int64_t pages,
+               int64_t table_rows, const void *x, const void *W,
+               const int64_t *positions, const int64_t *slots,
+               const float *cos_sin, const void *y, const void *kv_cache,
+               int read_indices);
+
+/* Static text for a status code (never NULL). */
+const char *qkvf_strerror(int status);
+
+/*
+ * The launch shape of (N, M): grid blocks of the projection kernel, the
+ * split of K across blocks, waves per block and 16-row tiles per block.
+ * A pure function of its arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or
+ * QKVF_ERR_ROWS.  Any output pointer may be NULL.
+ */
+int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block,
+              int *tiles_per_block);
+
+/* Bytes of the device workspace qkvf_prepare allocates per device. */
+size_t qkvf_workspace_bytes(void);
+
+/* Free the workspace of every device and forget prepared shapes.  No call
+ * may be in flight. */
+void qkvf_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKVF_H */

@@ -1,1 +1,137 @@
-"""libqkvfront: the decode-batch attention front on MI355X (gfx950)."""
+"""libqkvfront: the decode-batch attention front on MI355X (gfx950).
+
+A thin ctypes binding of the C ABI declared in include/qkvf.h.  Every step
+of the front runs in the HIP kernels of libqkvfront.so; this module only
+passes device pointers, sizes and the current stream.  It raises if the
+library is not built: there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqkvfront.so")
+
+HIDDEN = 8192
+HEAD_DIM = 64
+QHEADS_PER_KV = 8
+PAGE_SLOTS = 16
+SLOT_WIDTH = 128
+MAX_ROWS = 16
+
+STATUS = {
+    0: "QKVF_OK", 1: "QKVF_ERR_DEVICE", 2: "QKVF_ERR_SHAPE", 3: "QKVF_ERR_ROWS",
+    4: "QKVF_ERR_ALIGN", 5: "QKVF_ERR_NULLPTR", 6: "QKVF_ERR_NOT_PREPARED",
+    7: "QKVF_ERR_ALLOC", 8: "QKVF_ERR_HIP", 9: "QKVF_ERR_RANGE",
+    10: "QKVF_ERR_OVERLAP", 11: "QKVF_ERR_MEMORY",
+}
+EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
+           "qkvf_workspace_bytes", "qkvf_release")
+
+
+class QkvfError(ValueError):
+    """A call the library refused; .status is the qkvf_status code."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        self.code = STATUS.get(status, str(status))
+        super().__init__(f"{what}: {self.code}: {strerror(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqkvfront.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m kv_insert_amd.build` "
+                           "or __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.qkvf_prepare.argtypes = [I, I, I]
+    L.qkvf_prepare.restype = I
+    L.qkvf_run.argtypes = [P, P, P, P, P, P, P, I, P]
+    L.qkvf_run.restype = I
+    L.qkvf_check.argtypes = [I, I, I, I64, I64, P, P, P, P, P, P, P, I]
+    L.qkvf_check.restype = I
+    L.qkvf_strerror.argtypes = [I]
+    L.qkvf_strerror.restype = ctypes.c_char_p
+    L.qkvf_plan.argtypes = [I, I, P, P, P, P]
+    L.qkvf_plan.restype = I
+    L.qkvf_workspace_bytes.argtypes = []
+    L.qkvf_workspace_bytes.restype = ctypes.c_size_t
+    L.qkvf_release.argtypes = []
+    L.qkvf_release.restype = None
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().qkvf_strerror(int(status)).decode()
+
+
+def n_cols(num_kv_heads: int) -> int:
+    return 2 * (QHEADS_PER_KV * num_kv_heads + num_kv_heads) * HEAD_DIM
+
+
+def _raise(status: int, what: str):
+    if status != 0:
+        raise QkvfError(status, what)
+
+
+def prepare(N: int, num_kv_heads: int, M: int = MAX_ROWS) -> None:
+    """qkvf_prepare: ready (N, num_kv_heads) for row counts 1..M on the
+    current device and bind it as this thread's shape."""
+    _raise(lib().qkvf_prepare(int(N), int(num_kv_heads), int(M)), "qkvf_prepare")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def run(x, W, positions, slots, cos_sin, y, kv_cache, M: int | None = None, stream=None) -> None:
+    """qkvf_run on torch device tensors; enqueues on `stream` (default: the
+    current torch stream).  Shapes are the caller's contract (see qkvf_check)."""
+    M = x.shape[0] if M is None else int(M)
+    st = lib().qkvf_run(_ptr(x), _ptr(W), _ptr(positions), _ptr(slots), _ptr(cos_sin),
+                        _ptr(y), _ptr(kv_cache), M, _stream_handle(stream))
+    _raise(st, "qkvf_run")
+
+
+def check(x, W, positions, slots, cos_sin, y, kv_cache, num_kv_heads: int,
+          M: int | None = None, read_indices: bool = True) -> int:
+    """qkvf_check on torch tensors; returns the status code (0 = ok)."""
+    M = x.shape[0] if M is None else int(M)
+    N = W.shape[0]
+    pages = kv_cache.shape[0]
+    rows = 0 if cos_sin is None else cos_sin.shape[0]
+    return lib().qkvf_check(int(N), int(num_kv_heads), M, int(pages), int(rows), _ptr(x),
+                            _ptr(W), _ptr(positions), _ptr(slots), _ptr(cos_sin), _ptr(y),
+                            _ptr(kv_cache), 1 if read_indices else 0)
+
+
+def plan(N: int, M: int) -> dict:
+    """qkvf_plan: the launch shape of (N, M)."""
+    vals = [ctypes.c_int() for _ in range(4)]
+    _raise(lib().qkvf_plan(int(N), int(M), *[ctypes.byref(v) for v in vals]), "qkvf_plan")
+    return dict(zip(("grid", "k_splits", "waves_per_block", "tiles_per_block"),
+                    (v.value for v in vals)))
+
+
+def workspace_bytes() -> int:
+    return int(lib().qkvf_workspace_bytes())
+
+
+def release() -> None:
+    lib().qkvf_release()

@@ -1,0 +1,266 @@
+// C-ABI layer of libqkvfront: argument checks, per-device workspace and the
+// thread's bound shape.  The checks follow the reasons the reference front
+// refuses a call (qkv_front page, functions "unsupported", "hidden_rows_ok",
+// "supports_shape", "kv_cache_layout_ok"; cute_ops page, supports_call and
+// unsupported_projection); each becomes a status code.
+#include "qkvf.h"
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "qkvf_internal.h"
+
+namespace {
+
+using namespace qkvf;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    float *ws = nullptr;
+    int arch_ok = -1;                 // -1 unknown, 0 not gfx950, 1 gfx950
+    unsigned prepared[9] = {};        // per nkv: bit m set once rows m are prepared
+};
+
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+
+// Shape bound by the last qkvf_prepare of this thread.
+thread_local int t_N = 0;
+thread_local int t_nkv = 0;
+
+bool valid_nkv(int nkv) { return nkv == 1 || nkv == 2 || nkv == 4 || nkv == 8; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int shape_status(int N, int nkv, int M)
+{
+    if (!valid_nkv(nkv) || N != cols_for(nkv))
+        return QKVF_ERR_SHAPE;
+    if (M < 1 || M > kMaxRows)
+        return QKVF_ERR_ROWS;
+    return QKVF_OK;
+}
+
+// Current device index, with its gfx950 check cached.  Locks g_mu.
+int current_device(int *dev_out)
+{
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0)
+        return QKVF_ERR_DEVICE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKVF_ERR_DEVICE;
+    DeviceState &st = g_dev[dev];
+    if (st.arch_ok < 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return QKVF_ERR_DEVICE;
+        st.arch_ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    }
+    if (!st.arch_ok)
+        return QKVF_ERR_DEVICE;
+    *dev_out = dev;
+    return QKVF_OK;
+}
+
+int pointer_on_device(const void *p, int dev)
+{
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+        return QKVF_ERR_MEMORY;
+    }
+    const bool device_mem = attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+    if (!device_mem || attr.device != dev)
+        return QKVF_ERR_MEMORY;
+    return QKVF_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+Range range_of(const void *p, size_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+
+}  // namespace
+
+extern "C" {
+
+int qkvf_prepare(int N, int num_kv_heads, int M)
+{
+    const int s = shape_status(N, num_kv_heads, M);
+    if (s != QKVF_OK)
+        return s;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    const int ds = current_device(&dev);
+    if (ds != QKVF_OK)
+        return ds;
+    DeviceState &st = g_dev[dev];
+    if (st.ws == nullptr) {
+        void *p = nullptr;
+        if (hipMalloc(&p, kWorkspaceFloats * sizeof(float)) != hipSuccess) {
+            (void)hipGetLastError();
+            return QKVF_ERR_ALLOC;
+        }
+        st.ws = static_cast<float *>(p);
+    }
+    st.prepared[num_kv_heads] |= (2u << M) - 2u;  // rows 1..M
+    t_N = N;
+    t_nkv = num_kv_heads;
+    return QKVF_OK;
+}
+
+int qkvf_run(const void *x, const void *W, const int64_t *positions, const int64_t *slots,
+             const float *cos_sin, void *y, void *kv_cache, int M, hipStream_t stream)
+{
+    if (t_nkv == 0)
+        return QKVF_ERR_NOT_PREPARED;
+    if (M < 1 || M > kMaxRows)
+        return QKVF_ERR_ROWS;
+    if (!x || !W || !positions || !slots || !y || !kv_cache)
+        return QKVF_ERR_NULLPTR;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16) || !aligned(kv_cache, 16) ||
+        !aligned(cos_sin, 16) || !aligned(positions, 8) || !aligned(slots, 8))
+        return QKVF_ERR_ALIGN;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKVF_ERR_DEVICE;
+    const DeviceState &st = g_dev[dev];
+    if (st.ws == nullptr || !(st.prepared[t_nkv] & (1u << M)))
+        return QKVF_ERR_NOT_PREPARED;
+    const hipError_t e = launch_front(t_nkv, M, x, W, positions, slots, cos_sin, y, kv_cache,
+                                      st.ws, stream);
+    return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
+}
+
+int qkvf_check(int N, int num_kv_heads, int M, int64_t pages, int64_t table_rows,
+               const void *x, const void *W, const int64_t *positions, const int64_t *slots,
+               const float *cos_sin, const void *y, const void *kv_cache, int read_indices)
+{
+    int s = shape_status(N, num_kv_heads, M);
+    if (s != QKVF_OK)
+        return s;
+    if (!x || !W || !positions || !slots || !y || !kv_cache)
+        return QKVF_ERR_NULLPTR;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16) || !aligned(kv_cache, 16) ||
+        !aligned(cos_sin, 16) || !aligned(positions, 8) || !aligned(slots, 8))
+        return QKVF_ERR_ALIGN;
+    if (pages < 1 || (cos_sin != nullptr && table_rows < 1))
+        return QKVF_ERR_RANGE;
+    int dev = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        s = current_device(&dev);
+    }
+    if (s != QKVF_OK)
+        return s;
+    const void *ptrs[] = {x, W, positions, slots, y, kv_cache, cos_sin};
+    for (const void *p : ptrs) {
+        if (p == nullptr)
+            continue;
+        s = pointer_on_device(p, dev);
+        if (s != QKVF_OK)
+            return s;
+    }
+    const Range ry = range_of(y, size_t(M) * N * 2);
+    const Range rc = range_of(kv_cache, size_t(pages) * num_kv_heads * kPageSlots * kSlotWidth * 2);
+    const Range ins[] = {
+        range_of(x, size_t(M) * kHidden * 2), range_of(W, size_t(N) * kHidden * 2),
+        range_of(positions, size_t(M) * 8), range_of(slots, size_t(M) * 8),
+        cos_sin ? range_of(cos_sin, size_t(table_rows) * kHeadDim * 4) : Range{0, 0}};
+    if (overlap(ry, rc))
+        return QKVF_ERR_OVERLAP;
+    for (const Range &r : ins)
+        if (overlap(ry, r) || overlap(rc, r))
+            return QKVF_ERR_OVERLAP;
+    if (read_indices) {
+        std::vector<int64_t> pos(M), sl(M);
+        if (hipMemcpy(pos.data(), positions, M * sizeof(int64_t), hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(sl.data(), slots, M * sizeof(int64_t), hipMemcpyDeviceToHost) != hipSuccess) {
+            (void)hipGetLastError();
+            return QKVF_ERR_HIP;
+        }
+        for (int m = 0; m < M; ++m) {
+            if (cos_sin != nullptr && (pos[m] < 0 || pos[m] >= table_rows))
+                return QKVF_ERR_RANGE;
+            if (sl[m] >= pages * kPageSlots)
+                return QKVF_ERR_RANGE;
+        }
+        std::vector<int64_t> used;
+        for (int64_t v : sl)
+            if (v >= 0)
+                used.push_back(v);
+        std::sort(used.begin(), used.end());
+        if (std::adjacent_find(used.begin(), used.end()) != used.end())
+            return QKVF_ERR_RANGE;
+    }
+    return QKVF_OK;
+}
+
+const char *qkvf_strerror(int status)
+{
+    switch (status) {
+    case QKVF_OK: return "ok";
+    case QKVF_ERR_DEVICE: return "no current HIP device, or it is not gfx950 (MI355X)";
+    case QKVF_ERR_SHAPE: return "num_kv_heads must be 1, 2, 4 or 8 and N must be 1152 * num_kv_heads";
+    case QKVF_ERR_ROWS: return "M must be in [1, 16]";
+    case QKVF_ERR_ALIGN: return "x, W, y, kv_cache and cos_sin must be 16-byte aligned, positions and slots 8-byte aligned";
+    case QKVF_ERR_NULLPTR: return "a required pointer is NULL";
+    case QKVF_ERR_NOT_PREPARED: return "qkvf_prepare has not been called for this shape and row count on this thread and device";
+    case QKVF_ERR_ALLOC: return "the device workspace could not be allocated";
+    case QKVF_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case QKVF_ERR_RANGE: return "a position or slot is out of range, or a slot repeats";
+    case QKVF_ERR_OVERLAP: return "y or kv_cache overlaps another operand";
+    case QKVF_ERR_MEMORY: return "a pointer is not device memory of the current device";
+    default: return "unknown qkvf status";
+    }
+}
+
+int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block, int *tiles_per_block)
+{
+    int nkv = 0;
+    for (int c : {1, 2, 4, 8})
+        if (N == cols_for(c))
+            nkv = c;
+    if (nkv == 0)
+        return QKVF_ERR_SHAPE;
+    if (M < 1 || M > kMaxRows)
+        return QKVF_ERR_ROWS;
+    if (grid) *grid = kGrid;
+    if (k_splits) *k_splits = splits_for(nkv);
+    if (waves_per_block) *waves_per_block = kWaves;
+    if (tiles_per_block) *tiles_per_block = kTilesPerBlock;
+    return QKVF_OK;
+}
+
+size_t qkvf_workspace_bytes(void) { return kWorkspaceFloats * sizeof(float); }
+
+void qkvf_release(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    for (int d = 0; d < kMaxDevices; ++d) {
+        DeviceState &st = g_dev[d];
+        if (st.ws != nullptr) {
+            (void)hipSetDevice(d);
+            (void)hipFree(st.ws);
+        }
+        st = DeviceState{};
+    }
+    if (cur >= 0)
+        (void)hipSetDevice(cur);
+    t_N = 0;
+    t_nkv = 0;
+}
+
+}  // extern "C"

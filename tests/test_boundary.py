@@ -1,0 +1,126 @@
+"""The C-ABI boundary without a GPU: the library loads, exports what the
+header declares, and refuses malformed calls with the documented status
+before touching a device."""
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+import kv_insert_amd as qf
+from kv_insert_amd import build as qbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkvf.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if qbuild.is_stale():
+        qbuild.build()
+    return qf.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qkvf_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(qf.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {qf.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    pairs = dict((int(v), k) for k, v in re.findall(r"(QKVF_[A-Z_]+)\s*=\s*(\d+)", text))
+    assert pairs == qf.STATUS
+
+
+def test_strerror_is_distinct_text(L):
+    texts = [qf.strerror(s) for s in qf.STATUS]
+    assert all(texts) and len(set(texts)) == len(texts)
+    assert qf.strerror(999) == "unknown qkvf status"
+
+
+@pytest.mark.parametrize("nkv", [1, 2, 4, 8])
+def test_plan_is_a_function_of_shape(L, nkv):
+    N = qf.n_cols(nkv)
+    for M in (1, 8, 16):
+        p = qf.plan(N, M)
+        assert p == {"grid": 256, "k_splits": 32 // nkv, "waves_per_block": 8,
+                     "tiles_per_block": 9}
+        # every W row tile and every K split is covered exactly once
+        assert p["grid"] * p["tiles_per_block"] == (N // 16) * p["k_splits"]
+
+
+def test_plan_rejects_bad_shapes(L):
+    with pytest.raises(qf.QkvfError) as e:
+        qf.plan(1000, 4)
+    assert e.value.code == "QKVF_ERR_SHAPE"
+    for M in (0, 17, -1):
+        with pytest.raises(qf.QkvfError) as e:
+            qf.plan(1152, M)
+        assert e.value.code == "QKVF_ERR_ROWS"
+
+
+def test_workspace_size_is_constant(L):
+    # fp32 partials [splits][16 rows][N] with splits * N = 36864 for every nkv
+    assert qf.workspace_bytes() == 36864 * 16 * 4
+
+
+@pytest.mark.parametrize("N,nkv,M,code", [
+    (1152, 3, 4, 2), (2304, 1, 4, 2), (9216, 8, 0, 3), (9216, 8, 17, 3),
+    (1153, 1, 1, 2), (0, 0, 1, 2),
+])
+def test_prepare_rejects_bad_shapes_before_the_device(L, N, nkv, M, code):
+    assert L.qkvf_prepare(N, nkv, M) == code
+
+
+def test_run_without_prepare_is_refused(L):
+    res = []
+
+    def fresh_thread():  # the bound shape is per thread
+        res.append(L.qkvf_run(16, 16, 16, 16, 16, 16, 16, 1, None))
+
+    t = threading.Thread(target=fresh_thread)
+    t.start()
+    t.join()
+    assert res == [6]
+
+
+def test_check_refuses_in_order(L):
+    P = 1 << 20  # aligned stand-in addresses; never dereferenced
+    good = dict(x=P, W=2 * P, positions=3 * P, slots=4 * P, cos_sin=5 * P, y=6 * P,
+                kv_cache=7 * P)
+
+    def chk(N=9216, nkv=8, M=8, pages=16, rows=16, **kw):
+        a = dict(good, **kw)
+        return L.qkvf_check(N, nkv, M, pages, rows, a["x"], a["W"], a["positions"],
+                            a["slots"], a["cos_sin"], a["y"], a["kv_cache"], 0)
+
+    assert chk(N=9215) == 2
+    assert chk(M=0) == 3
+    for name in ("x", "W", "positions", "slots", "y", "kv_cache"):
+        assert chk(**{name: None}) == 5, name
+    for name in ("x", "W", "y", "kv_cache", "cos_sin"):
+        assert chk(**{name: good[name] + 8}) == 4, name
+    for name in ("positions", "slots"):
+        assert chk(**{name: good[name] + 4}) == 4, name
+    assert chk(pages=0) == 9
+
+
+def test_no_device_here_means_device_error(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.qkvf_prepare(1152, 1, 1) == 1
