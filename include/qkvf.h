@@ -59,7 +59,7 @@ typedef enum {
  * Prepare the front for N output columns, num_kv_heads KV heads and every
  * row count 1..M on the current device (qkv_front page, function "prepare":
  * ready the variants before graph capture).  Validates the shape, checks the
- * device is gfx950, allocates the device workspace once (2.25 MiB, the same
+ * device is gfx950, allocates the device workspace once (about 2.3 MB, the same
  * for every shape), and binds (N, num_kv_heads) as the calling thread's
  * current shape, which qkvf_run uses.  Call it again to switch shape; it is
  * cheap after the first call.  Not to be called during graph capture.

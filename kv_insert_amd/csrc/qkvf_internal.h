@@ -25,8 +25,13 @@ constexpr int cols_for(int nkv) { return 2 * (kQPerKv + 1) * nkv * kHeadDim; }
 // tile-splits for every supported nkv.
 constexpr int splits_for(int nkv) { return 32 / nkv; }
 
-// fp32 partials [splits][16][N]: splits * N = 36864 for every nkv.
-constexpr size_t kWorkspaceFloats = size_t(32) * 1152 * kMaxRows;
+// Workspace layout (floats): fp32 partials [splits][M][N] (splits * N = 36864
+// for every nkv, M <= 16), then the gathered cos|sin rows [16][64], then the
+// slots as int64 [16].
+constexpr size_t kPartialFloats = size_t(32) * 1152 * kMaxRows;
+constexpr size_t kAuxRowsOffset = kPartialFloats;
+constexpr size_t kAuxSlotsOffset = kAuxRowsOffset + size_t(kMaxRows) * kHeadDim;
+constexpr size_t kWorkspaceFloats = kAuxSlotsOffset + size_t(kMaxRows) * 2;
 
 // Enqueue the projection partials and the epilogue on `stream`.  Shapes were
 // validated by the caller; ws holds kWorkspaceFloats floats on this device.
