@@ -42,7 +42,7 @@ extern "C" {
  * "unsupported"; cute_ops page, supports_call and unsupported_projection). */
 typedef enum {
     QKVF_OK = 0,
-    QKVF_ERR_DEVICE = 1,        /* no current device, or it is not gfx950 */
+    QKVF_ERR_DEVICE = 1,        /* no current device, not gfx950, or fewer than 256 CUs */
     QKVF_ERR_SHAPE = 2,         /* num_kv_heads not in {1,2,4,8} or N != 1152*num_kv_heads */
     QKVF_ERR_ROWS = 3,          /* M outside [1, 16] */
     QKVF_ERR_ALIGN = 4,         /* a pointer is not aligned as stated below */
@@ -52,15 +52,18 @@ typedef enum {
     QKVF_ERR_HIP = 8,           /* a HIP runtime call or a launch failed */
     QKVF_ERR_RANGE = 9,         /* qkvf_check: a position or slot out of range, duplicate slots */
     QKVF_ERR_OVERLAP = 10,      /* qkvf_check: an output overlaps another operand */
-    QKVF_ERR_MEMORY = 11        /* qkvf_check: a pointer is not device memory of the current device */
+    QKVF_ERR_MEMORY = 11,       /* qkvf_check: a pointer is not device memory of the current device */
+    QKVF_ERR_TIMEOUT = 12       /* qkvf_device_fault: a call gave up waiting for a partial result */
 } qkvf_status;
 
 /*
  * Prepare the front for N output columns, num_kv_heads KV heads and every
  * row count 1..M on the current device (qkv_front page, function "prepare":
  * ready the variants before graph capture).  Validates the shape, checks the
- * device is gfx950, allocates the device workspace once (about 2.3 MB, the same
- * for every shape), and binds (N, num_kv_heads) as the calling thread's
+ * device is gfx950 with room for the kernel's 256 blocks at once (one per
+ * CU), allocates and zeroes the device workspace once (about 2.4 MB, the same
+ * for every shape; it synchronizes the device then), and binds
+ * (N, num_kv_heads) as the calling thread's
  * current shape, which qkvf_run uses.  Call it again to switch shape; it is
  * cheap after the first call.  Not to be called during graph capture.
  * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS, QKVF_ERR_DEVICE, QKVF_ERR_ALLOC.
@@ -88,8 +91,12 @@ int qkvf_prepare(int N, int num_kv_heads, int M);
  * distinct non-negative slots, and no overlap between y, kv_cache and the
  * inputs (qkvf_check verifies all of these).  The call allocates nothing,
  * never synchronizes and only enqueues work on `stream` (so it can be
- * captured in a HIP graph).  Calls on one device share its workspace: they
- * must be ordered (one stream, or streams ordered by events).
+ * captured in a HIP graph, and replayed any number of times).  Calls on one
+ * device share its workspace and need all 256 CUs: they must be ordered (one
+ * stream, or streams ordered by events) and not overlap other calls of this
+ * library on the device.  A call that cannot make progress (calls
+ * overlapped) gives up after a bounded wait, leaves invalid outputs and
+ * records a fault that qkvf_device_fault reports.
  * Errors (cheap scalar checks only): QKVF_ERR_NOT_PREPARED, QKVF_ERR_ROWS,
  * QKVF_ERR_NULLPTR, QKVF_ERR_ALIGN, QKVF_ERR_DEVICE, QKVF_ERR_HIP.
  */
@@ -128,6 +135,15 @@ int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block,
 
 /* Bytes of the device workspace qkvf_prepare allocates per device. */
 size_t qkvf_workspace_bytes(void);
+
+/*
+ * Synchronize the current device and report whether any call on it since the
+ * last query gave up waiting for a partial result (QKVF_ERR_TIMEOUT; the
+ * outputs of that call are not valid).  Clears the record.  Returns QKVF_OK
+ * when no call failed (or nothing was prepared on the device), QKVF_ERR_HIP
+ * on a runtime error.
+ */
+int qkvf_device_fault(void);
 
 /* Free the workspace of every device and forget prepared shapes.  No call
  * may be in flight. */

@@ -24,10 +24,10 @@ STATUS = {
     0: "QKVF_OK", 1: "QKVF_ERR_DEVICE", 2: "QKVF_ERR_SHAPE", 3: "QKVF_ERR_ROWS",
     4: "QKVF_ERR_ALIGN", 5: "QKVF_ERR_NULLPTR", 6: "QKVF_ERR_NOT_PREPARED",
     7: "QKVF_ERR_ALLOC", 8: "QKVF_ERR_HIP", 9: "QKVF_ERR_RANGE",
-    10: "QKVF_ERR_OVERLAP", 11: "QKVF_ERR_MEMORY",
+    10: "QKVF_ERR_OVERLAP", 11: "QKVF_ERR_MEMORY", 12: "QKVF_ERR_TIMEOUT",
 }
 EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
-           "qkvf_workspace_bytes", "qkvf_release")
+           "qkvf_workspace_bytes", "qkvf_device_fault", "qkvf_release")
 
 
 class QkvfError(ValueError):
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.qkvf_plan.restype = I
     L.qkvf_workspace_bytes.argtypes = []
     L.qkvf_workspace_bytes.restype = ctypes.c_size_t
+    L.qkvf_device_fault.argtypes = []
+    L.qkvf_device_fault.restype = I
     L.qkvf_release.argtypes = []
     L.qkvf_release.restype = None
     _lib = L
@@ -131,6 +133,12 @@ def plan(N: int, M: int) -> dict:
 
 def workspace_bytes() -> int:
     return int(lib().qkvf_workspace_bytes())
+
+
+def device_fault() -> int:
+    """qkvf_device_fault: synchronize; 0, or QKVF_ERR_TIMEOUT if a call on the
+    current device gave up waiting (its outputs are then invalid)."""
+    return int(lib().qkvf_device_fault())
 
 
 def release() -> None:

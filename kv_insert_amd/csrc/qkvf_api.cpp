@@ -105,11 +105,26 @@ int qkvf_prepare(int N, int num_kv_heads, int M)
     if (ds != QKVF_OK)
         return ds;
     DeviceState &st = g_dev[dev];
+    // The kernel's blocks hand partials to each other, so all of them must be
+    // resident at once: one per CU on the full 256-CU device.
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        blocks_per_cu(num_kv_heads) * cus < kGrid) {
+        (void)hipGetLastError();
+        return QKVF_ERR_DEVICE;
+    }
     if (st.ws == nullptr) {
         void *p = nullptr;
         if (hipMalloc(&p, kWorkspaceFloats * sizeof(float)) != hipSuccess) {
             (void)hipGetLastError();
             return QKVF_ERR_ALLOC;
+        }
+        // Epoch, fault word and ready flags start at zero.
+        if (hipMemset(p, 0, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(p);
+            return QKVF_ERR_HIP;
         }
         st.ws = static_cast<float *>(p);
     }
@@ -210,7 +225,7 @@ const char *qkvf_strerror(int status)
 {
     switch (status) {
     case QKVF_OK: return "ok";
-    case QKVF_ERR_DEVICE: return "no current HIP device, or it is not gfx950 (MI355X)";
+    case QKVF_ERR_DEVICE: return "no current HIP device, or it is not a gfx950 (MI355X) with 256 CUs free for one projection block each";
     case QKVF_ERR_SHAPE: return "num_kv_heads must be 1, 2, 4 or 8 and N must be 1152 * num_kv_heads";
     case QKVF_ERR_ROWS: return "M must be in [1, 16]";
     case QKVF_ERR_ALIGN: return "x, W, y, kv_cache and cos_sin must be 16-byte aligned, positions and slots 8-byte aligned";
@@ -221,6 +236,7 @@ const char *qkvf_strerror(int status)
     case QKVF_ERR_RANGE: return "a position or slot is out of range, or a slot repeats";
     case QKVF_ERR_OVERLAP: return "y or kv_cache overlaps another operand";
     case QKVF_ERR_MEMORY: return "a pointer is not device memory of the current device";
+    case QKVF_ERR_TIMEOUT: return "a call on this device waited too long for a partial result (calls overlapped or the device was shared) and its output is not valid";
     default: return "unknown qkvf status";
     }
 }
@@ -243,6 +259,32 @@ int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block, int 
 }
 
 size_t qkvf_workspace_bytes(void) { return kWorkspaceFloats * sizeof(float); }
+
+int qkvf_device_fault(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKVF_ERR_DEVICE;
+    DeviceState &st = g_dev[dev];
+    if (st.ws == nullptr)
+        return QKVF_OK;
+    unsigned word = 0;
+    unsigned *fault = reinterpret_cast<unsigned *>(st.ws) + kFaultWord;
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(&word, fault, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKVF_ERR_HIP;
+    }
+    if (word == 0)
+        return QKVF_OK;
+    const unsigned zero = 0;
+    if (hipMemcpy(fault, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKVF_ERR_HIP;
+    }
+    return QKVF_ERR_TIMEOUT;
+}
 
 void qkvf_release(void)
 {

@@ -25,19 +25,31 @@ constexpr int cols_for(int nkv) { return 2 * (kQPerKv + 1) * nkv * kHeadDim; }
 // tile-splits for every supported nkv.
 constexpr int splits_for(int nkv) { return 32 / nkv; }
 
-// Workspace layout (floats): fp32 partials [splits][M][N] (splits * N = 36864
-// for every nkv, M <= 16), then the gathered cos|sin rows [16][64], then the
-// slots as int64 [16].
-constexpr size_t kPartialFloats = size_t(32) * 1152 * kMaxRows;
-constexpr size_t kAuxRowsOffset = kPartialFloats;
-constexpr size_t kAuxSlotsOffset = kAuxRowsOffset + size_t(kMaxRows) * kHeadDim;
-constexpr size_t kWorkspaceFloats = kAuxSlotsOffset + size_t(kMaxRows) * 2;
+// Workspace layout (32-bit words): tagged partials [splits][M][N] as 64-bit
+// words {fp32 partial, call number} (splits * N = 36864 for every nkv,
+// M <= 16), then a sticky fault word, then one flag per projection block
+// that counts the calls the block has finished.
+constexpr size_t kPartialWords = size_t(32) * 1152 * kMaxRows;  // 64-bit words
+constexpr size_t kFaultWord = 2 * kPartialWords;
+constexpr size_t kReadyOffset = kFaultWord + 64;
+constexpr size_t kWorkspaceFloats = kReadyOffset + kGrid;
 
-// Enqueue the projection partials and the epilogue on `stream`.  Shapes were
-// validated by the caller; ws holds kWorkspaceFloats floats on this device.
+// Iterations (each with a short sleep) a wave waits for a partial before it
+// gives up and records a fault; far longer than any call takes.
+constexpr unsigned kSpinLimit = 1u << 20;
+
+// Fault word values.
+constexpr unsigned kFaultTimeout = 1;
+
+// Enqueue one front call on `stream`.  Shapes were validated by the caller;
+// ws holds kWorkspaceFloats words on this device, zeroed before first use.
 hipError_t launch_front(int nkv, int M, const void *x, const void *W,
                         const int64_t *positions, const int64_t *slots,
                         const float *cos_sin, void *y, void *kv_cache,
                         float *ws, hipStream_t stream);
+
+// Projection blocks of the front kernel for nkv that one CU can hold at once
+// (0 on error).  The kernel needs all kGrid blocks resident together.
+int blocks_per_cu(int nkv);
 
 }  // namespace qkvf

@@ -65,6 +65,7 @@ def run_gpu(case: Case, g=None, label: str = "") -> dict:
     qf.run(g["x"], g["W"], g["positions"], g["slots"], g["cos_sin"], g["y"], g["kv_cache"],
            M=case.M)
     torch.cuda.synchronize()
+    assert qf.device_fault() == 0, "a call gave up waiting for a partial"
     return g
 
 

@@ -74,9 +74,9 @@ def test_plan_rejects_bad_shapes(L):
 
 
 def test_workspace_size_is_constant(L):
-    # fp32 partials [splits][16 rows][N] with splits * N = 36864 for every nkv,
-    # then 16 gathered cos|sin rows of 64 floats and 16 int64 slots
-    assert qf.workspace_bytes() == 36864 * 16 * 4 + 16 * 64 * 4 + 16 * 8
+    # 64-bit tagged partials [splits][16 rows][N] with splits * N = 36864 for
+    # every nkv, then 64 words (fault word, padding) and 256 call counters
+    assert qf.workspace_bytes() == 36864 * 16 * 8 + 64 * 4 + 256 * 4
 
 
 @pytest.mark.parametrize("N,nkv,M,code", [

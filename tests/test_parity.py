@@ -179,3 +179,37 @@ def test_run_refuses_unprepared_row_count():
     qf.prepare(1152, 1, 16)
     run_gpu(case, g, label="after prepare")
     check(case, g)
+
+
+def test_graph_capture_and_replays():
+    """One call captured in a HIP graph and replayed with new inputs copied
+    into its buffers, with eager calls and synchronizations in between; every
+    replay matches the oracle (the per-call epoch keeps replays apart)."""
+    w = wl.C2
+    cases = [Case(w, s) for s in range(3)]
+    g = cases[0].device()
+    qf.prepare(w.N, w.nkv, w.M)
+    say("graph capture")
+    qf.run(g["x"], g["W"], g["positions"], g["slots"], g["cos_sin"], g["y"], g["kv_cache"])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        qf.run(g["x"], g["W"], g["positions"], g["slots"], g["cos_sin"], g["y"], g["kv_cache"])
+    other = Case(wl.sweep(4, 1))
+    go = other.device()
+    for rep in range(4):
+        c = cases[rep % 3]
+        for k in ("x", "W", "positions", "slots"):
+            g[k].copy_(getattr(c, k).to("cuda"))
+        g["kv_cache"].copy_(c.cache.to("cuda"))
+        g["y"].view(torch.int16).fill_(CANARY)
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert qf.device_fault() == 0
+        check(c, g)
+        # eager work of another shape between replays
+        run_gpu(other, go, label=f"eager between replays {rep}")
+        check(other, go)
+        qf.prepare(w.N, w.nkv, w.M)
