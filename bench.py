@@ -12,6 +12,7 @@ in HBM.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,19 +28,43 @@ import kv_insert_amd as qf  # noqa: E402
 from kv_insert_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "kv_insert_amd", "csrc", "qkvf_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "front_fused_counters.json")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(w) -> float | None:
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    recorded in profiles/, if they were taken on the kernel as it is now."""
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    entry = rec.get("workloads", {}).get(w.name)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=wl.C3.name,
                     help="one of " + ", ".join(wl.WORKLOADS) + " or sweep_m<M>_nkv<K>")
     ap.add_argument("--wsets", type=int, default=0, help="override rotated weight sets")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--repeats", type=int, default=3, help="timed repeats; the median is kept")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every workload and sweep point; one JSON line each on stderr")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
+                    help="instead of the front, time device-to-device copies of MB megabytes "
+                         "(a plain copy kernel of known size, for scaling memory counters)")
     return ap.parse_args()
 
 
@@ -102,6 +127,60 @@ def cpu_baseline(w: wl.Workload, budget_s: float) -> dict | None:
             "sample": f"{calls} full oracle calls of {w.name} (weight set 0), {threads} OpenMP threads"}
 
 
+def time_front(w: wl.Workload, sets: int, steps: int, warmup: int, repeats: int):
+    pool = Pool(w, sets)
+    qf.prepare(w.N, w.nkv, w.M)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            pool.call(i, stream)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        # HIP events on the stream the kernel is launched on: one launch per
+        # call, so elapsed / steps is the average launch duration.
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            pool.call(warmup + i, stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / steps)  # ms per call
+    fault = qf.device_fault()
+    if fault != 0:
+        raise RuntimeError(f"a timed call gave up waiting for a partial: {qf.strerror(fault)}")
+    del pool
+    torch.cuda.empty_cache()
+    return sorted(times)[len(times) // 2], times
+
+
+def rotated_sets(w: wl.Workload, requested: int) -> int:
+    sets = requested or w.wsets
+    # enough weight sets that the rotation exceeds the 256 MB MALL
+    return max(sets, int(600e6 // (w.N * wl.HIDDEN * 2)) + 1)
+
+
+def copy_calibration(mb: float, steps: int) -> None:
+    n = int(mb * 1e6) // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "steps": steps,
+                      "ms_per_copy": round(ms, 6)}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -111,38 +190,31 @@ def main():
         sys.exit(2)
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
-    w = workload_by_name(a.workload)
-    sets = a.wsets or w.wsets
-    if sets < 2 and w.N * wl.HIDDEN * 2 * sets < 300e6:
-        # a single small weight set would sit in the 256 MB MALL: rotate
-        # enough sets to exceed it
-        sets = max(sets, int(600e6 // (w.N * wl.HIDDEN * 2)) + 1)
     torch.cuda.set_device(0)
-    pool = Pool(w, sets)
-    qf.prepare(w.N, w.nkv, w.M)
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        for i in range(a.warmup):
-            pool.call(i, stream)
-    torch.cuda.synchronize()
-
-    times = []
-    for rep in range(a.repeats):
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(a.steps):
-            pool.call(a.warmup + i, stream)
-        end.record(stream)
-        torch.cuda.synchronize()
-        times.append(start.elapsed_time(end) / a.steps)  # ms per call
-    ms = sorted(times)[len(times) // 2]
+    if a.copy_calibration > 0:
+        copy_calibration(a.copy_calibration, a.steps)
+        return
+    w = workload_by_name(a.workload)
+    sets = rotated_sets(w, a.wsets)
+    ms, times = time_front(w, sets, a.steps, a.warmup, a.repeats)
     nbytes = w.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
+    if a.all:
+        others = list(wl.WORKLOADS.values()) + [wl.sweep(m, k) for k in wl.SWEEP_NKV
+                                                for m in wl.SWEEP_M]
+        for o in others:
+            oms, _ = time_front(o, rotated_sets(o, 0), a.steps, a.warmup, a.repeats)
+            ogbs = o.algorithmic_bytes() / (oms * 1e-3) / 1e9
+            print(json.dumps({"workload": o.name, "M": o.M, "num_kv_heads": o.nkv, "N": o.N,
+                              "us_per_call": round(oms * 1e3, 3), "GB_per_s": round(ogbs, 1),
+                              "frac_of_8TBs": round(ogbs / HBM_PEAK_GBS, 4),
+                              "weight_sets_rotated": rotated_sets(o, 0)}),
+                  file=sys.stderr, flush=True)
     base = cpu_baseline(w, a.cpu_baseline_seconds)
+    traffic = measured_traffic(w)
     out = {
-        "metric": "QKV-front achieved HBM GB/s (algorithmic bytes per call / time per call)",
+        "metric": "QKV-front achieved HBM GB/s (algorithmic bytes per call / time per call); "
+                  "us_per_call alongside, fraction of peak in roofline.frac",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -157,9 +229,10 @@ def main():
         "data": "synthetic",
         "config": dict(wl.describe(w), weight_sets_rotated=sets,
                        algorithmic_bytes_per_call=nbytes),
-        "roofline": {"bound": "hbm", "kernel": "front (projection + epilogue, whole call)",
+        "roofline": {"bound": "hbm", "kernel": f"front_fused<{w.nkv}> (the whole call)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic)},
         "cpu_baseline": base,
         "repeats_ms": [round(t, 6) for t in times],
     }
