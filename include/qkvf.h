@@ -61,8 +61,9 @@ typedef enum {
  * row count 1..M on the current device (qkv_front page, function "prepare":
  * ready the variants before graph capture).  Validates the shape, checks the
  * device is gfx950 with room for the kernel's 256 blocks at once (one per
- * CU), allocates and zeroes the device workspace once (about 2.4 MB, the same
- * for every shape; it synchronizes the device then), and binds
+ * CU), allocates and zeroes the device workspace once (about 4.7 MB, the same
+ * for every shape) and checks on which XCD each block runs (both synchronize
+ * the device, once), and binds
  * (N, num_kv_heads) as the calling thread's
  * current shape, which qkvf_run uses.  Call it again to switch shape; it is
  * cheap after the first call.  Not to be called during graph capture.
@@ -135,6 +136,18 @@ int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block,
 
 /* Bytes of the device workspace qkvf_prepare allocates per device. */
 size_t qkvf_workspace_bytes(void);
+
+/*
+ * How the kernel's blocks hand partial sums to each other.  mode 0 (the
+ * default): a partial read on the XCD that produced it is stored plainly and
+ * read from that XCD's L2, when qkvf_prepare found that the device places a
+ * kernel's blocks on its 8 XCDs round robin (checked once per device with a
+ * small kernel; if not, mode 1 is used).  mode 1: every partial is written through to memory.
+ * Both modes give bitwise the same results; mode 1 is a little slower.  For
+ * diagnostics and tests; applies to calls launched afterwards, process-wide.
+ * Returns QKVF_OK, or QKVF_ERR_RANGE for another mode.
+ */
+int qkvf_set_handoff(int mode);
 
 /*
  * Synchronize the current device and report whether any call on it since the

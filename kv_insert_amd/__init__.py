@@ -27,7 +27,7 @@ STATUS = {
     10: "QKVF_ERR_OVERLAP", 11: "QKVF_ERR_MEMORY", 12: "QKVF_ERR_TIMEOUT",
 }
 EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
-           "qkvf_workspace_bytes", "qkvf_device_fault", "qkvf_release")
+           "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_device_fault", "qkvf_release")
 
 
 class QkvfError(ValueError):
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.qkvf_plan.restype = I
     L.qkvf_workspace_bytes.argtypes = []
     L.qkvf_workspace_bytes.restype = ctypes.c_size_t
+    L.qkvf_set_handoff.argtypes = [I]
+    L.qkvf_set_handoff.restype = I
     L.qkvf_device_fault.argtypes = []
     L.qkvf_device_fault.restype = I
     L.qkvf_release.argtypes = []
@@ -133,6 +135,12 @@ def plan(N: int, M: int) -> dict:
 
 def workspace_bytes() -> int:
     return int(lib().qkvf_workspace_bytes())
+
+
+def set_handoff(mode: int) -> None:
+    """qkvf_set_handoff: 0 = partials stay in the producing XCD's L2 where the
+    placement allows (default), 1 = always write through (same results)."""
+    _raise(lib().qkvf_set_handoff(int(mode)), "qkvf_set_handoff")
 
 
 def device_fault() -> int:

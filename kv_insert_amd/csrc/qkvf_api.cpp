@@ -23,11 +23,13 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
     float *ws = nullptr;
     int arch_ok = -1;                 // -1 unknown, 0 not gfx950, 1 gfx950
+    bool round_robin = false;         // blocks with equal b % 8 verified to share an XCD
     unsigned prepared[9] = {};        // per nkv: bit m set once rows m are prepared
 };
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
+bool g_force_coherent = false;        // qkvf_set_handoff(1)
 
 // Shape bound by the last qkvf_prepare of this thread.
 thread_local int t_N = 0;
@@ -127,6 +129,16 @@ int qkvf_prepare(int N, int num_kv_heads, int M)
             return QKVF_ERR_HIP;
         }
         st.ws = static_cast<float *>(p);
+        // Where do the kernel's blocks run?  If round robin over the XCDs,
+        // blocks with equal b % 8 share an XCD, and a partial read by one of
+        // them may stay in that XCD's L2.
+        bool rr = false;
+        if (check_placement(reinterpret_cast<unsigned *>(st.ws) + kPlacementOffset, &rr) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            return QKVF_ERR_HIP;
+        }
+        st.round_robin = rr;
     }
     st.prepared[num_kv_heads] |= (2u << M) - 2u;  // rows 1..M
     t_N = N;
@@ -152,8 +164,9 @@ int qkvf_run(const void *x, const void *W, const int64_t *positions, const int64
     const DeviceState &st = g_dev[dev];
     if (st.ws == nullptr || !(st.prepared[t_nkv] & (1u << M)))
         return QKVF_ERR_NOT_PREPARED;
+    const bool coherent = g_force_coherent || !st.round_robin;
     const hipError_t e = launch_front(t_nkv, M, x, W, positions, slots, cos_sin, y, kv_cache,
-                                      st.ws, stream);
+                                      st.ws, coherent, stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }
 
@@ -236,7 +249,7 @@ const char *qkvf_strerror(int status)
     case QKVF_ERR_RANGE: return "a position or slot is out of range, or a slot repeats";
     case QKVF_ERR_OVERLAP: return "y or kv_cache overlaps another operand";
     case QKVF_ERR_MEMORY: return "a pointer is not device memory of the current device";
-    case QKVF_ERR_TIMEOUT: return "a call on this device waited too long for a partial result (calls overlapped or the device was shared) and its output is not valid";
+    case QKVF_ERR_TIMEOUT: return "a call on this device gave up waiting for a partial result (calls overlapped, or the device placed blocks on XCDs differently than at prepare) and its output is not valid";
     default: return "unknown qkvf status";
     }
 }
@@ -259,6 +272,15 @@ int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block, int 
 }
 
 size_t qkvf_workspace_bytes(void) { return kWorkspaceFloats * sizeof(float); }
+
+int qkvf_set_handoff(int mode)
+{
+    if (mode != 0 && mode != 1)
+        return QKVF_ERR_RANGE;
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_force_coherent = mode == 1;
+    return QKVF_OK;
+}
 
 int qkvf_device_fault(void)
 {

@@ -28,25 +28,34 @@ constexpr int splits_for(int nkv) { return 32 / nkv; }
 // Workspace layout (32-bit words): tagged partials [splits][M][N] as 64-bit
 // words {fp32 partial, call number} (splits * N = 36864 for every nkv,
 // M <= 16), then a sticky fault word, then one flag per projection block
-// that counts the calls the block has finished.
+// that counts the calls the block has finished, then scratch words for the
+// placement check.
 constexpr size_t kPartialWords = size_t(32) * 1152 * kMaxRows;  // 64-bit words
 constexpr size_t kFaultWord = 2 * kPartialWords;
 constexpr size_t kReadyOffset = kFaultWord + 64;
-constexpr size_t kWorkspaceFloats = kReadyOffset + kGrid;
+constexpr size_t kPlacementOffset = kReadyOffset + kGrid;  // scratch of check_placement
+constexpr size_t kWorkspaceFloats = kPlacementOffset + kGrid;
 
 // Iterations (each with a short sleep) a wave waits for a partial before it
 // gives up and records a fault; far longer than any call takes.
 constexpr unsigned kSpinLimit = 1u << 20;
 
 // Fault word values.
-constexpr unsigned kFaultTimeout = 1;
+constexpr unsigned kFaultTimeout = 1;    // a wait gave up
 
 // Enqueue one front call on `stream`.  Shapes were validated by the caller;
 // ws holds kWorkspaceFloats words on this device, zeroed before first use.
+// coherent: every partial is stored write-through (the safe mode when the
+// blocks with equal b % 8 are not known to share an XCD).
 hipError_t launch_front(int nkv, int M, const void *x, const void *W,
                         const int64_t *positions, const int64_t *slots,
                         const float *cos_sin, void *y, void *kv_cache,
-                        float *ws, hipStream_t stream);
+                        float *ws, bool coherent, hipStream_t stream);
+
+// Launch a kGrid-block kernel on the current device, one block per CU, and
+// report whether blocks were placed on XCDs round robin (block b on XCD
+// (b + c) % 8 for some c).  scratch holds kGrid words.  Synchronous.
+hipError_t check_placement(unsigned *scratch, bool *round_robin);
 
 // Projection blocks of the front kernel for nkv that one CU can hold at once
 // (0 on error).  The kernel needs all kGrid blocks resident together.

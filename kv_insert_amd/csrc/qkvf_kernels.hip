@@ -21,10 +21,11 @@
 //    the block's fp32 partial goes to the workspace, each value stored
 //    together with the number of the call in one 64-bit word.
 //
-//  Epilogue: each (pair of heads, token) is one item of one wave.  The wave
-//    fetched its token's slot and cos|sin row while the weights streamed; it
-//    reads the S partials of each of its columns until all carry this call's
-//    number (a bounded wait), sums them in
+//  Epilogue: each (head, pair of tokens) is one item of one wave, on the XCD
+//    whose blocks produced that head's partials.  The wave fetched its
+//    tokens' slots and cos|sin rows while the weights streamed; it reads the
+//    S partials of each of its columns until all carry this call's number (a
+//    bounded wait, normally served by the XCD's own L2), sums them in
 //    split order, rounds to bf16 (round to nearest even), applies to q and k
 //    heads the weightless RMS norm (sum of squares by a butterfly of lane
 //    exchanges) and the interleaved rotation, and stores its part of y and of
@@ -52,6 +53,13 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor word 3 for raw 32-bit buffer access, and the cache bits
+// of a device-coherent (sc1) buffer load: it is served by the XCD's L2 when
+// the writer ran on the same XCD, and sees other XCDs' write-through stores.
+constexpr int kBufferConfig = 0x00020000;
+constexpr int kCacheSc1 = 16;
 
 constexpr float kEps = 1e-6f;
 
@@ -99,12 +107,11 @@ __global__ void __launch_bounds__(kWaves * 64, 1)
 front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const int64_t *__restrict__ positions, const int64_t *__restrict__ slots,
             const float *__restrict__ cos_sin, __bf16 *__restrict__ y,
-            __bf16 *__restrict__ kv_cache, float *__restrict__ ws, int M)
+            __bf16 *__restrict__ kv_cache, float *__restrict__ ws, int M, int coherent)
 {
     using Sh = Shape<NKV>;
     constexpr int ST = Sh::STEPS, D = Sh::DEPTH, U = kTilesPerBlock, C = Sh::CHUNKS;
     constexpr int LD = Sh::LOADS, N = Sh::N, NQ = kQPerKv * NKV;
-    constexpr int PAIRS = N / (2 * kHeadDim);  // epilogue items per token
     constexpr size_t kTileStride = size_t(kTileRows) * kHidden;
     __shared__ __attribute__((aligned(16))) unsigned char lds[Sh::LDS_BYTES];
 
@@ -118,24 +125,39 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // previous call.
     const unsigned target =
         __hip_atomic_load(ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-    const int split = b % Sh::S;
-    const int group = b / Sh::S;
+    // Blocks are dispatched to the 8 XCDs round robin: block b runs on XCD
+    // (b + c) % 8 for a c that varies between launches.  So the 32 blocks
+    // with b % 8 == x share one XCD; they take the S splits of row groups
+    // x*NKV .. x*NKV + NKV - 1, rows [144 NKV x, 144 NKV (x + 1)), and the
+    // partials of a head stay in that XCD's L2 (for NKV >= 4 every head; for
+    // smaller NKV heads can straddle two XCDs).
+    const int xcd = b & 7;
+    const int slot_in_xcd = b >> 3;
+    const int split = slot_in_xcd % Sh::S;
+    const int group = xcd * NKV + slot_in_xcd / Sh::S;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;   // A row (W row in the tile) and B column (token)
     const int q = lane >> 4;   // which 8 of the 32 K values of a step
     const int k0 = split * Sh::KB;
+    constexpr int XCD_ROWS = N / 8;  // rows of W whose partials one XCD produces
 
-    // This wave's epilogue item, if any: head pair `pair` of token `tok`.
-    const int item = wave * kGrid + b;
-    const bool has_item = item < PAIRS * M;
-    const int tok = has_item ? item / PAIRS : 0;
-    const int pair = item - tok * PAIRS;
-    const int pi = lane & 31;  // rotation pair within the lane's head
-    // Unconditional loads (tok < M always), so nothing waits on them until
-    // they are used.
-    const int64_t pos_t = positions[tok];
-    const int64_t slot_t = slots[tok];
+    // This wave's epilogue item, if any: head `head` for tokens 2 tp (lanes
+    // 0-31) and 2 tp + 1 (lanes 32-63), among the heads whose first row lies
+    // in this XCD's rows; lane pi of each half owns rotation pair pi.
+    const int head_lo = (XCD_ROWS * xcd + kHeadDim - 1) / kHeadDim;
+    const int head_hi = (XCD_ROWS * (xcd + 1) + kHeadDim - 1) / kHeadDim;
+    const int tpairs = (M + 1) >> 1;
+    const int item = wave * (kGrid / 8) + slot_in_xcd;
+    const bool has_item = item < (head_hi - head_lo) * tpairs;
+    const int head = head_lo + (has_item ? item / tpairs : 0);
+    const int tok = 2 * (has_item ? item % tpairs : 0) + (lane >> 5);
+    const bool tok_ok = tok < M;
+    const int tok_c = tok_ok ? tok : M - 1;  // keeps the idle half's loads in bounds
+    const int pi = lane & 31;
+    // Unconditional loads, so nothing waits on them until they are used.
+    const int64_t pos_t = positions[tok_c];
+    const int64_t slot_t = slots[tok_c];
 
     // Chunk (8 K values) of this lane's operands in MFMA step st, relative to
     // k0: A (W) and B (x) use the same chunk, so the MFMA contracts matching
@@ -224,9 +246,17 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         for (int w = 1; w < kWaves; ++w)
             sum += red[w][u][t][row];
         const int n = (group * U + u) * kTileRows + row;
-        __hip_atomic_store(parts + (size_t(split) * M + t) * N + n,
-                           (uint64_t(target) << 32) | __float_as_uint(sum), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t word = (uint64_t(target) << 32) | __float_as_uint(sum);
+        uint64_t *dst = parts + (size_t(split) * M + t) * N + n;
+        // The reader of row n runs on the XCD holding its head's first row.
+        // On this XCD a plain store is enough (the reader's device-coherent
+        // load is served by the shared L2); for another XCD the store writes
+        // through to memory.
+        const int reader_xcd = (n / kHeadDim) * kHeadDim / XCD_ROWS;
+        if (!coherent && reader_xcd == xcd)
+            *dst = word;
+        else
+            __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // Count this call in the block's flag (read back at the next call's start).
@@ -234,23 +264,28 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         __hip_atomic_store(ready + b, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     if (has_item) {
-        // The S partials of this lane's two columns, each tagged with the
-        // call that wrote it: poll (bounded) until every tag is this call's,
-        // then sum in split order.
-        const int h = 2 * pair + (lane >> 5);  // head of this half-wave
-        const int n = h * kHeadDim + 2 * pi;
-        const uint64_t *src = parts + size_t(tok) * N + n;
-        constexpr size_t kSplitStride = size_t(N);  // times M, below
-        uint64_t v[Sh::S][2];
+        // The S partials of this lane's two columns, each tagged with the call
+        // that wrote it: poll (bounded) with device-coherent loads until every
+        // tag is this call's, then sum in split order.  A stale word never
+        // carries this call's tag.
+        const int n = head * kHeadDim + 2 * pi;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            parts, 0, int(sizeof(uint64_t) * kPartialWords), kBufferConfig);
+        const int base = (tok_c * N + n) * int(sizeof(uint64_t));
+        constexpr int kSplitBytes = int(sizeof(uint64_t)) * N;  // times M, below
+        u32x2 v[Sh::S][2];
         for (unsigned tries = 0;; ++tries) {
+            // Every round must issue its loads again: keep the compiler from
+            // hoisting them out of the loop.
+            asm volatile("" ::: "memory");
             bool mine = true;
 #pragma unroll
-            for (int s = 0; s < Sh::S; ++s)
+            for (int sp = 0; sp < Sh::S; ++sp)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    v[s][c] = __hip_atomic_load(src + size_t(s) * M * kSplitStride + c,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    mine = mine && unsigned(v[s][c] >> 32) == target;
+                    const int off = base + sp * M * kSplitBytes + c * int(sizeof(uint64_t));
+                    v[sp][c] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, kCacheSc1);
+                    mine = mine && v[sp][c].y == target;
                 }
             if (__all(mine))
                 break;
@@ -262,9 +297,9 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         }
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int s = 0; s < Sh::S; ++s) {
-            a0 += __uint_as_float(unsigned(v[s][0]));
-            a1 += __uint_as_float(unsigned(v[s][1]));
+        for (int sp = 0; sp < Sh::S; ++sp) {
+            a0 += __uint_as_float(v[sp][0].x);
+            a1 += __uint_as_float(v[sp][1].x);
         }
         const __bf16 p0 = __bf16(a0), p1 = __bf16(a1);
         const float f0 = float(p0), f1 = float(p1);
@@ -280,6 +315,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             rc = 1.f;
             rs = 0.f;
         }
+        const int h = head;
         __bf16 o0 = p0, o1 = p1;
         if (h < NQ + NKV) {  // q and k heads
             const float rr = rsqrtf(ss * (1.0f / kHeadDim) + kEps);
@@ -288,9 +324,10 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             o1 = __bf16(n1 * rc + n0 * rs);
         }
         const unsigned packed = pack2(o0, o1);
-        *reinterpret_cast<unsigned *>(y + size_t(tok) * N + n) = packed;
+        if (tok_ok)
+            *reinterpret_cast<unsigned *>(y + size_t(tok) * N + n) = packed;
 
-        if (slot_t >= 0 && h >= NQ && h < NQ + 2 * NKV) {
+        if (tok_ok && slot_t >= 0 && h >= NQ && h < NQ + 2 * NKV) {
             const int64_t page = slot_t / kPageSlots, off = slot_t % kPageSlots;
             const bool is_k = h < NQ + NKV;
             const int j = is_k ? h - NQ : h - NQ - NKV;
@@ -305,13 +342,25 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
 template <int NKV>
 hipError_t launch(int M, const void *x, const void *W, const int64_t *positions,
                   const int64_t *slots, const float *cos_sin, void *y, void *kv_cache,
-                  float *ws, hipStream_t stream)
+                  float *ws, bool coherent, hipStream_t stream)
 {
     hipLaunchKernelGGL(front_fused<NKV>, dim3(kGrid), dim3(kWaves * 64), 0, stream,
                        static_cast<const __bf16 *>(x), static_cast<const __bf16 *>(W),
                        positions, slots, cos_sin, static_cast<__bf16 *>(y),
-                       static_cast<__bf16 *>(kv_cache), ws, M);
+                       static_cast<__bf16 *>(kv_cache), ws, M, coherent ? 1 : 0);
     return hipGetLastError();
+}
+
+// One block per CU, like the front kernel; each records the XCD it runs on.
+__global__ void __launch_bounds__(kWaves * 64) where_blocks_run(unsigned *out)
+{
+    __shared__ float pad[16384];  // 64 KB
+    pad[threadIdx.x] = 0.f;
+    __syncthreads();
+    unsigned hw_xcd;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(hw_xcd));
+    if (threadIdx.x == 0)
+        out[blockIdx.x] = hw_xcd + (pad[1] == 0.f ? 0u : 1u);
 }
 
 template <int NKV>
@@ -331,15 +380,34 @@ int occupancy()
 hipError_t launch_front(int nkv, int M, const void *x, const void *W,
                         const int64_t *positions, const int64_t *slots,
                         const float *cos_sin, void *y, void *kv_cache, float *ws,
-                        hipStream_t stream)
+                        bool coherent, hipStream_t stream)
 {
     switch (nkv) {
-    case 1: return launch<1>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, stream);
-    case 2: return launch<2>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, stream);
-    case 4: return launch<4>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, stream);
-    case 8: return launch<8>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, stream);
+    case 1: return launch<1>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
+    case 2: return launch<2>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
+    case 4: return launch<4>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
+    case 8: return launch<8>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t check_placement(unsigned *scratch, bool *round_robin)
+{
+    hipLaunchKernelGGL(where_blocks_run, dim3(kGrid), dim3(kWaves * 64), 0, nullptr, scratch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    unsigned host[kGrid];
+    e = hipMemcpy(host, scratch, sizeof host, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return e;
+    // A rotation: block b on XCD (b + c) % 8 for one c.
+    const unsigned c = (host[0] + 8) % 8;
+    bool ok = host[0] < 8;
+    for (int b = 0; b < kGrid; ++b)
+        ok = ok && host[b] == (unsigned(b) + c) % 8;
+    *round_robin = ok;
+    return hipSuccess;
 }
 
 int blocks_per_cu(int nkv)

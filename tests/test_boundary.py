@@ -75,8 +75,9 @@ def test_plan_rejects_bad_shapes(L):
 
 def test_workspace_size_is_constant(L):
     # 64-bit tagged partials [splits][16 rows][N] with splits * N = 36864 for
-    # every nkv, then 64 words (fault word, padding) and 256 call counters
-    assert qf.workspace_bytes() == 36864 * 16 * 8 + 64 * 4 + 256 * 4
+    # every nkv, then 64 words (fault word, padding), 256 call counters and
+    # 256 scratch words
+    assert qf.workspace_bytes() == 36864 * 16 * 8 + 64 * 4 + 256 * 4 + 256 * 4
 
 
 @pytest.mark.parametrize("N,nkv,M,code", [
@@ -118,6 +119,13 @@ def test_check_refuses_in_order(L):
     for name in ("positions", "slots"):
         assert chk(**{name: good[name] + 4}) == 4, name
     assert chk(pages=0) == 9
+
+
+def test_set_handoff_modes(L):
+    assert L.qkvf_set_handoff(2) == 9
+    assert L.qkvf_set_handoff(-1) == 9
+    assert L.qkvf_set_handoff(1) == 0
+    assert L.qkvf_set_handoff(0) == 0
 
 
 def test_no_device_here_means_device_error(L):

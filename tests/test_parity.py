@@ -213,3 +213,20 @@ def test_graph_capture_and_replays():
         run_gpu(other, go, label=f"eager between replays {rep}")
         check(other, go)
         qf.prepare(w.N, w.nkv, w.M)
+
+
+@pytest.mark.parametrize("w", [wl.C2, wl.C3, wl.sweep(16, 1), wl.sweep(5, 2), wl.sweep(16, 4)],
+                         ids=lambda w: w.name)
+def test_write_through_handoff_is_bitwise_identical(w):
+    """Both hand-off modes give the same bits (and match the oracle)."""
+    case = Case(w)
+    g0 = run_gpu(case, label=f"{w.name} default hand-off")
+    y0, c0 = g0["y"].clone(), g0["kv_cache"].clone()
+    try:
+        qf.set_handoff(1)
+        g1 = run_gpu(case, label=f"{w.name} write-through hand-off")
+    finally:
+        qf.set_handoff(0)
+    check(case, g1)
+    assert torch.equal(y0.view(torch.int16), g1["y"].view(torch.int16))
+    assert torch.equal(c0.view(torch.int16), g1["kv_cache"].view(torch.int16))
