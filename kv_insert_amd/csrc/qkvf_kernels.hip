@@ -17,9 +17,10 @@
 //        the block's K range, and issues v_mfma_f32_16x16x32_bf16 with W as
 //        the 16-row A operand and the tokens (x, held in registers for the
 //        whole kernel, zero past M) as the 16 B columns.
-//    The 8 wave partials of each tile are summed in LDS in wave order and
-//    the block's fp32 partial goes to the workspace, each value stored
-//    together with the number of the call in one 64-bit word.
+//    The 8 wave partials of each tile are summed in LDS in wave order, one
+//    tile behind the stream, and the block's fp32 partial goes to the
+//    workspace, each value stored together with the number of the call in
+//    one 64-bit word.
 //
 //  Epilogue: each (head, pair of tokens) is one item of one wave, on the XCD
 //    whose blocks produced that head's partials.  The wave fetched its
@@ -53,7 +54,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer descriptor word 3 for raw 32-bit buffer access, and the cache bits
 // of a device-coherent (sc1) buffer load: it is served by the XCD's L2 when
@@ -74,9 +75,11 @@ struct Shape {
     static constexpr int CHUNKS = KB / 8;          // 16-byte chunks per tile row
     static constexpr int LOADS = 2 * CHUNKS / 64;  // 1 KB loads per wave per tile (2 rows)
     static constexpr int TILE_BYTES = kTileRows * KB * 2;
-    // The wave partials of all tiles, summed at the end, reuse the same LDS.
-    static constexpr int RED_BYTES = 4 * kWaves * kTilesPerBlock * kTileRows * (kTileRows + 1);
-    static constexpr int LDS_BYTES = 2 * TILE_BYTES > RED_BYTES ? 2 * TILE_BYTES : RED_BYTES;
+    // Double-buffered tile; for NKV <= 2 also the wave partials of all 9
+    // tiles, summed after the loop in the same LDS.
+    static constexpr int ALL_PARTIALS = 4 * kTilesPerBlock * kWaves * kTileRows * (kTileRows + 1);
+    static constexpr int LDS_BYTES =
+        NKV >= 4 || 2 * TILE_BYTES >= ALL_PARTIALS ? 2 * TILE_BYTES : ALL_PARTIALS;
     // Tiles of loads in flight per wave: up to 12 loads of 1 KB per wave.
     static constexpr int DEPTH = (12 / LOADS) < kTilesPerBlock ? (12 / LOADS) : kTilesPerBlock;
     static_assert(S * GROUPS == kGrid, "grid covers every (split, group)");
@@ -201,50 +204,13 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     float rc = cs_row[pi], rs = cs_row[32 + pi];
     __builtin_amdgcn_sched_barrier(0);
 
-    f32x4 acc[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        unsigned char *tile = lds + (u & 1) * Sh::TILE_BYTES;
-#pragma unroll
-        for (int j = 0; j < LD; ++j)
-            *reinterpret_cast<bf16x8 *>(tile + loff[j]) = ring[u % D][j];
-        if (u + D < U) {
-#pragma unroll
-            for (int j = 0; j < LD; ++j)
-                ring[u % D][j] = stream16(wtile + (u + D) * kTileStride + goff[j]);
-        }
-        __syncthreads();
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < ST; ++st) {
-            const int c = chunk_of(st);
-            const bf16x8 w = *reinterpret_cast<const bf16x8 *>(tile + (r * C + (c ^ r)) * 16);
-            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xv[st], a, 0, 0, 0);
-        }
-        acc[u] = a;
-    }
-
-    // Lane (r, q) holds D[row = 4q + v][token = r], v = 0..3.  Sum the 8
-    // waves' partials of every tile in wave order through LDS (reusing the
-    // tile buffers) and write the block's partial ws[split][token][n].
-    float(*red)[U][kTileRows][kTileRows + 1] =
-        reinterpret_cast<float(*)[U][kTileRows][kTileRows + 1]>(lds);
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            red[wave][u][r][4 * q + v] = acc[u][v];
-    __syncthreads();
-    const int per_tile = kTileRows * M;
-    for (int e = threadIdx.x; e < U * per_tile; e += kWaves * 64) {
-        const int u = e / per_tile;
-        const int rem = e - u * per_tile;
-        const int t = rem >> 4, row = rem & 15;
-        float sum = red[0][u][t][row];
+    // Store the block's partial of (tile u, token t, row): the sum of the 8
+    // waves' partials slab[w][t][row] in wave order (slab: [8][16][17]).
+    auto store_partial = [&](const float *slab, int u, int t, int row) {
+        float sum = slab[t * (kTileRows + 1) + row];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
-            sum += red[w][u][t][row];
+            sum += slab[(w * kTileRows + t) * (kTileRows + 1) + row];
         const int n = (group * U + u) * kTileRows + row;
         const uint64_t word = (uint64_t(target) << 32) | __float_as_uint(sum);
         uint64_t *dst = parts + (size_t(split) * M + t) * N + n;
@@ -257,6 +223,76 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             *dst = word;
         else
             __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    constexpr int SLAB = kWaves * kTileRows * (kTileRows + 1);  // floats per tile
+
+    // Large tiles (NKV >= 4) reduce each tile inside the loop, where LDS has
+    // spare bandwidth: the 8 wave partials of tile u go to red[u & 1] right
+    // after its MFMAs and, one barrier later (all waves have written them),
+    // are summed and stored while tile u + 1 streams; red[u & 1] is written
+    // again only after the barrier that follows the sum.  Small tiles keep
+    // the loop short and reduce all tiles after it.  Lane (r, q) holds
+    // D[row = 4q + v][token = r], v = 0..3; token columns r >= M are never
+    // needed.
+    constexpr bool kReduceInLoop = NKV >= 4;
+    __shared__ float red[kReduceInLoop ? 2 : 1][kReduceInLoop ? SLAB : 1];
+    f32x4 acc[kReduceInLoop ? 1 : U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        unsigned char *tile = lds + (u & 1) * Sh::TILE_BYTES;
+#pragma unroll
+        for (int j = 0; j < LD; ++j)
+            *reinterpret_cast<bf16x8 *>(tile + loff[j]) = ring[u % D][j];
+        if (u + D < U) {
+#pragma unroll
+            for (int j = 0; j < LD; ++j)
+                ring[u % D][j] = stream16(wtile + (u + D) * kTileStride + goff[j]);
+        }
+        __syncthreads();
+        if constexpr (kReduceInLoop) {
+            if (u > 0 && threadIdx.x < kTileRows * M)
+                store_partial(red[(u - 1) & 1], u - 1, threadIdx.x >> 4, threadIdx.x & 15);
+        }
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < ST; ++st) {
+            const int c = chunk_of(st);
+            const bf16x8 w = *reinterpret_cast<const bf16x8 *>(tile + (r * C + (c ^ r)) * 16);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xv[st], a, 0, 0, 0);
+        }
+        if constexpr (kReduceInLoop) {
+            if (r < M) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[u & 1][(wave * kTileRows + r) * (kTileRows + 1) + 4 * q + v] = a[v];
+            }
+        } else {
+            acc[u] = a;
+        }
+    }
+    if constexpr (kReduceInLoop) {
+        __syncthreads();
+        if (threadIdx.x < kTileRows * M)
+            store_partial(red[(U - 1) & 1], U - 1, threadIdx.x >> 4, threadIdx.x & 15);
+    } else {
+        // All tiles at once, in the tile buffers the loop no longer needs.
+        float *all = reinterpret_cast<float *>(lds);
+        static_assert(sizeof(float) * U * SLAB <= Sh::LDS_BYTES, "partials fit in LDS");
+        __syncthreads();
+        if (r < M) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    all[u * SLAB + (wave * kTileRows + r) * (kTileRows + 1) + 4 * q + v] = acc[u][v];
+        }
+        __syncthreads();
+        const int per_tile = kTileRows * M;
+        for (int e = threadIdx.x; e < U * per_tile; e += kWaves * 64) {
+            const int u = e / per_tile;
+            const int rem = e - u * per_tile;
+            store_partial(all + u * SLAB, u, rem >> 4, rem & 15);
+        }
     }
 
     // Count this call in the block's flag (read back at the next call's start).
@@ -273,21 +309,23 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             parts, 0, int(sizeof(uint64_t) * kPartialWords), kBufferConfig);
         const int base = (tok_c * N + n) * int(sizeof(uint64_t));
         constexpr int kSplitBytes = int(sizeof(uint64_t)) * N;  // times M, below
-        u32x2 v[Sh::S][2];
+        // One 16-byte load per split reads the two columns' words; each 8-byte
+        // half was stored whole and is checked on its own.
+        u32x4 v[Sh::S];
         for (unsigned tries = 0;; ++tries) {
             // Every round must issue its loads again: keep the compiler from
             // hoisting them out of the loop.
             asm volatile("" ::: "memory");
-            bool mine = true;
 #pragma unroll
             for (int sp = 0; sp < Sh::S; ++sp)
+                v[sp] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, base + sp * M * kSplitBytes, 0,
+                                                              kCacheSc1);
+            // All loads are in flight before any tag is looked at.
+            unsigned bad = 0;
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int off = base + sp * M * kSplitBytes + c * int(sizeof(uint64_t));
-                    v[sp][c] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, kCacheSc1);
-                    mine = mine && v[sp][c].y == target;
-                }
-            if (__all(mine))
+            for (int sp = 0; sp < Sh::S; ++sp)
+                bad |= (v[sp].y ^ target) | (v[sp].w ^ target);
+            if (__all(bad == 0))
                 break;
             if (tries >= kSpinLimit) {
                 words[kFaultWord] = kFaultTimeout;
@@ -298,8 +336,8 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int sp = 0; sp < Sh::S; ++sp) {
-            a0 += __uint_as_float(v[sp][0].x);
-            a1 += __uint_as_float(v[sp][1].x);
+            a0 += __uint_as_float(v[sp].x);
+            a1 += __uint_as_float(v[sp].z);
         }
         const __bf16 p0 = __bf16(a0), p1 = __bf16(a1);
         const float f0 = float(p0), f1 = float(p1);
