@@ -73,6 +73,10 @@ def _load():
     lib.qkvfo_front.restype = None
     lib.qkvfo_front.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_double, P, P, P, P, ctypes.c_int]
+    lib.qkvfo_attn2.restype = None
+    lib.qkvfo_attn2.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int,
+                                P, ctypes.c_int64, P, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_double, ctypes.c_double, P, ctypes.c_int64]
     _lib = lib
     return lib
 
@@ -180,3 +184,34 @@ def front(x, W, positions, slots, cos_sin, nkv: int, eps: float, kv_cache,
                     nkv, M, eps, _ptr(z), _ptr(p), _ptr(y), _ptr(kv_cache),
                     nthreads)
     return y, p
+
+
+ATTN2_SCALE = 0.125   # reading: 1 / sqrt(head_dim)
+ATTN2_EPS = 1e-6      # reading: the o-norm epsilon
+
+
+def attn2(q, gate, kv_cache, nkv: int, block_table, seq_lens, window: int = 0,
+          scale: float = ATTN2_SCALE, eps: float = ATTN2_EPS):
+    """Paged decode attention of 8 query rows per request with the o-norm and
+    sigmoid gate.  q, gate: uint16 [R*8, >= nq*64] (rows may be wider: only
+    the first nq*64 columns are read); kv_cache: uint16 [pages, nkv, 16,
+    128]; block_table: int32 [R, max_pages]; seq_lens: int32 [R].
+    Returns uint16 [R*8, nq*64]."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    gate = np.ascontiguousarray(gate, dtype=np.uint16)
+    kv = np.ascontiguousarray(kv_cache, dtype=np.uint16)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    R = sl.shape[0]
+    nq = QHEADS_PER_KV * nkv
+    assert q.shape[0] == R * 8 and gate.shape[0] == R * 8
+    assert q.shape[1] >= nq * HEAD_DIM and gate.shape[1] >= nq * HEAD_DIM
+    assert kv.shape[1:] == (nkv, PAGE_SLOTS, SLOT_WIDTH)
+    assert bt.shape[0] == R and np.all(sl >= 8)
+    assert int(sl.max()) <= bt.shape[1] * PAGE_SLOTS
+    out = np.empty((R * 8, nq * HEAD_DIM), dtype=np.uint16)
+    lib.qkvfo_attn2(_ptr(q), q.shape[1], _ptr(gate), gate.shape[1], _ptr(kv), nkv,
+                    _ptr(bt), bt.shape[1], _ptr(sl), R, int(window), scale, eps,
+                    _ptr(out), out.shape[1])
+    return out

@@ -205,3 +205,80 @@ void qkvfo_front(const uint16_t *x, const uint16_t *W, const int64_t *positions,
         p[i] = qkvfo_double_to_bf16(z_scratch[i]);
     qkvfo_epilogue(p, positions, slots, cos_sin, nkv, M, eps, y, kv_cache);
 }
+
+/*
+ * attn2: paged decode attention of the 8-token verify step, fused with the
+ * weightless RMS norm of its output and the sigmoid gate (cute_ops page,
+ * attn2 entry: head_dim 64, 8 query heads per KV head, bf16 cache
+ * [pages][nkv][16][128] with K | V per slot, 8 query rows per request, any
+ * context length L >= 8, optional sliding window).
+ *
+ * Request r has L = seq_lens[r] tokens; its 8 query rows are the last 8
+ * positions, row t at position p = L - 8 + t.  Key position k lives in slot
+ * k % 16 of physical page block_table[r * bt_stride + k / 16].  For query
+ * head h (KV head h / 8) the row attends keys k in [lo, p] with lo = 0, or
+ * lo = max(0, p - window + 1) when window > 0 (readings: causal inside the
+ * draft, a window of W keys ending at the row's own position):
+ *   s_k  = scale * q . K_k,   a = softmax(s),   o = sum_k a_k V_k,
+ *   out  = o / sqrt(mean(o^2) + eps) * sigmoid(gate),  rounded to bf16.
+ * q and gate rows are bf16 [R*8][nq*64] with row strides q_stride and
+ * gate_stride (elements); out likewise with out_stride.  All in double.
+ */
+void qkvfo_attn2(const uint16_t *q, int64_t q_stride, const uint16_t *gate,
+                 int64_t gate_stride, const uint16_t *kv_cache, int nkv,
+                 const int32_t *block_table, int64_t bt_stride,
+                 const int32_t *seq_lens, int R, int window, double scale,
+                 double eps, uint16_t *out, int64_t out_stride)
+{
+    const int nq = QHEADS_PER_KV * nkv;
+    for (int r = 0; r < R; ++r) {
+        const int L = seq_lens[r];
+        for (int t = 0; t < 8; ++t) {
+            const int64_t row = (int64_t)r * 8 + t;
+            const int p = L - 8 + t;
+            const int lo = window > 0 ? (p - window + 1 > 0 ? p - window + 1 : 0) : 0;
+            for (int h = 0; h < nq; ++h) {
+                const int j = h / QHEADS_PER_KV;
+                const uint16_t *qh = q + row * q_stride + (int64_t)h * HEAD_DIM;
+                double m = -INFINITY;
+                for (int k = lo; k <= p; ++k) {
+                    const int32_t page = block_table[(int64_t)r * bt_stride + k / PAGE_SLOTS];
+                    const uint16_t *K = kv_cache + (((int64_t)page * nkv + j) * PAGE_SLOTS + k % PAGE_SLOTS) * SLOT_WIDTH;
+                    double s = 0.0;
+                    for (int d = 0; d < HEAD_DIM; ++d)
+                        s += qkvfo_bf16_to_double(qh[d]) * qkvfo_bf16_to_double(K[d]);
+                    s *= scale;
+                    if (s > m)
+                        m = s;
+                }
+                double l = 0.0, o[HEAD_DIM];
+                for (int d = 0; d < HEAD_DIM; ++d)
+                    o[d] = 0.0;
+                for (int k = lo; k <= p; ++k) {
+                    const int32_t page = block_table[(int64_t)r * bt_stride + k / PAGE_SLOTS];
+                    const uint16_t *K = kv_cache + (((int64_t)page * nkv + j) * PAGE_SLOTS + k % PAGE_SLOTS) * SLOT_WIDTH;
+                    const uint16_t *V = K + HEAD_DIM;
+                    double s = 0.0;
+                    for (int d = 0; d < HEAD_DIM; ++d)
+                        s += qkvfo_bf16_to_double(qh[d]) * qkvfo_bf16_to_double(K[d]);
+                    const double a = exp(s * scale - m);
+                    l += a;
+                    for (int d = 0; d < HEAD_DIM; ++d)
+                        o[d] += a * qkvfo_bf16_to_double(V[d]);
+                }
+                double ss = 0.0;
+                for (int d = 0; d < HEAD_DIM; ++d) {
+                    o[d] /= l;
+                    ss += o[d] * o[d];
+                }
+                const double rr = 1.0 / sqrt(ss / HEAD_DIM + eps);
+                const uint16_t *g = gate + row * gate_stride + (int64_t)h * HEAD_DIM;
+                uint16_t *dst = out + row * out_stride + (int64_t)h * HEAD_DIM;
+                for (int d = 0; d < HEAD_DIM; ++d) {
+                    const double sg = 1.0 / (1.0 + exp(-qkvfo_bf16_to_double(g[d])));
+                    dst[d] = qkvfo_double_to_bf16(o[d] * rr * sg);
+                }
+            }
+        }
+    }
+}
