@@ -158,6 +158,61 @@ int qkvf_set_handoff(int mode);
  */
 int qkvf_device_fault(void);
 
+/*
+ * attn2: paged decode attention of the 8-token verify step fused with the
+ * weightless RMS norm of its output and the sigmoid gate, the input of the
+ * layer's o_proj (cute_ops page, attn2 entry).  Per request r with
+ * L = seq_lens[r] >= 8 tokens, query row t (0..7, row index 8 r + t) sits at
+ * position L - 8 + t; for each q head h (KV head h / 8) it attends the keys
+ * at positions lo .. L - 8 + t (lo = 0, or L - 8 + t - window + 1 clamped to
+ * 0 with a sliding window), whose K | V sit in slot k % 16 of physical page
+ * block_table[r * block_table_stride + k / 16] of the cache that
+ * qkvf_run fills.  With s = q K^T / 8 (softmax scale 1/sqrt(64)) and
+ * o = softmax(s) V, the output is o / sqrt(mean(o^2) + 1e-6) *
+ * sigmoid(gate), per head of 64 values, rounded to bf16.
+ *
+ * qkvf_attn2_prepare binds a layer's (num_kv_heads, max_model_len,
+ * max_reqs, window) to the calling thread (window 0: none; a window of at
+ * least max_model_len is none) and sizes the device workspace in which
+ * long-context calls split their keys (the split count depends on these
+ * values only, so the launch shape is fixed and capturable).  It may
+ * allocate and synchronize; no attn2 call may be in flight.
+ * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS (max_reqs outside [1, 64]),
+ * QKVF_ERR_DEVICE, QKVF_ERR_ALLOC.
+ */
+int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int window);
+
+/*
+ * Enqueue attn2 for num_reqs requests on `stream` (device pointers):
+ *   q         bf16 rows [8 num_reqs][>= 512 nkv] with row stride
+ *             q_row_stride elements: the q columns (for the front's output y,
+ *             q = y, stride N), 16-byte aligned, stride a multiple of 8;
+ *   gate      bf16 rows, the gate columns (y + 1152 nkv - 512 nkv for y), row
+ *             stride gate_row_stride (8-byte aligned, multiple of 4);
+ *   kv_cache  bf16 [pages][num_kv_heads][16][128], 16-byte aligned;
+ *   block_table int32 [num_reqs][block_table_stride] physical page numbers,
+ *             at least ceil(seq_lens[r] / 16) of them in row r;
+ *   seq_lens  int32 [num_reqs], each in [8, max_model_len] (the kernel clamps
+ *             a length outside that range, giving a meaningless result);
+ *   out       bf16 rows [8 num_reqs][512 nkv], row stride out_row_stride
+ *             (8-byte aligned, multiple of 4), written.
+ * The caller guarantees page numbers below the cache's page count and finite
+ * cache entries at the positions a row attends.  Allocates
+ * nothing, never synchronizes; calls on one device share its workspace and
+ * must be ordered.  Errors: QKVF_ERR_NOT_PREPARED, QKVF_ERR_ROWS,
+ * QKVF_ERR_NULLPTR, QKVF_ERR_SHAPE (a stride too small), QKVF_ERR_ALIGN,
+ * QKVF_ERR_DEVICE, QKVF_ERR_HIP.
+ */
+int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate,
+                   int64_t gate_row_stride, const void *kv_cache,
+                   const int32_t *block_table, int64_t block_table_stride,
+                   const int32_t *seq_lens, int num_reqs, void *out,
+                   int64_t out_row_stride, hipStream_t stream);
+
+/* The number of key splits attn2 uses for a layer (a pure function of its
+ * arguments).  Returns QKVF_OK or QKVF_ERR_SHAPE. */
+int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int *splits);
+
 /* Free the workspace of every device and forget prepared shapes.  No call
  * may be in flight. */
 void qkvf_release(void);

@@ -27,7 +27,8 @@ STATUS = {
     10: "QKVF_ERR_OVERLAP", 11: "QKVF_ERR_MEMORY", 12: "QKVF_ERR_TIMEOUT",
 }
 EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
-           "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_device_fault", "qkvf_release")
+           "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_device_fault", "qkvf_release",
+           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan")
 
 
 class QkvfError(ValueError):
@@ -68,6 +69,12 @@ def lib() -> ctypes.CDLL:
     L.qkvf_set_handoff.restype = I
     L.qkvf_device_fault.argtypes = []
     L.qkvf_device_fault.restype = I
+    L.qkvf_attn2_prepare.argtypes = [I, I, I, I]
+    L.qkvf_attn2_prepare.restype = I
+    L.qkvf_attn2_run.argtypes = [P, I64, P, I64, P, P, I64, P, I, P, I64, P]
+    L.qkvf_attn2_run.restype = I
+    L.qkvf_attn2_plan.argtypes = [I, I, I, P]
+    L.qkvf_attn2_plan.restype = I
     L.qkvf_release.argtypes = []
     L.qkvf_release.restype = None
     _lib = L
@@ -151,3 +158,28 @@ def device_fault() -> int:
 
 def release() -> None:
     lib().qkvf_release()
+
+
+def attn2_prepare(num_kv_heads: int, max_model_len: int, max_reqs: int, window: int = 0) -> None:
+    """qkvf_attn2_prepare: bind a layer's attn2 configuration to this thread."""
+    _raise(lib().qkvf_attn2_prepare(int(num_kv_heads), int(max_model_len), int(max_reqs),
+                                    int(window)), "qkvf_attn2_prepare")
+
+
+def attn2_run(q, gate, kv_cache, block_table, seq_lens, out, stream=None) -> None:
+    """qkvf_attn2_run on torch tensors: q, gate, out are 2-D bf16 views whose
+    rows are the 8 query rows of each request (row strides taken from the
+    views); block_table int32 [R, pages]; seq_lens int32 [R]."""
+    st = lib().qkvf_attn2_run(_ptr(q), q.stride(0), _ptr(gate), gate.stride(0), _ptr(kv_cache),
+                              _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+                              int(seq_lens.shape[0]), _ptr(out), out.stride(0),
+                              _stream_handle(stream))
+    _raise(st, "qkvf_attn2_run")
+
+
+def attn2_plan(num_kv_heads: int, max_model_len: int, window: int = 0) -> int:
+    """qkvf_attn2_plan: the number of key splits of the layer's launches."""
+    z = ctypes.c_int()
+    _raise(lib().qkvf_attn2_plan(int(num_kv_heads), int(max_model_len), int(window),
+                                 ctypes.byref(z)), "qkvf_attn2_plan")
+    return z.value

@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqkvfront.so")
-SOURCES = [os.path.join(CSRC, "qkvf_api.cpp"), os.path.join(CSRC, "qkvf_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "qkvf_api.cpp"), os.path.join(CSRC, "qkvf_kernels.hip"),
+           os.path.join(CSRC, "qkvf_attn2.hip")]
 HEADERS = [os.path.join(ROOT, "include", "qkvf.h"), os.path.join(CSRC, "qkvf_internal.h")]
 
 HIPCC_FLAGS = [

@@ -22,6 +22,8 @@ constexpr int kMaxDevices = 64;
 
 struct DeviceState {
     float *ws = nullptr;
+    float *attn2_ws = nullptr;        // split partials of attn2
+    size_t attn2_ws_floats = 0;
     int arch_ok = -1;                 // -1 unknown, 0 not gfx950, 1 gfx950
     bool round_robin = false;         // blocks with equal b % 8 verified to share an XCD
     unsigned prepared[9] = {};        // per nkv: bit m set once rows m are prepared
@@ -34,6 +36,12 @@ bool g_force_coherent = false;        // qkvf_set_handoff(1)
 // Shape bound by the last qkvf_prepare of this thread.
 thread_local int t_N = 0;
 thread_local int t_nkv = 0;
+
+// attn2 configuration bound by the last qkvf_attn2_prepare of this thread.
+struct Attn2Config {
+    int nkv = 0, max_model_len = 0, max_reqs = 0, window = 0, splits = 0;
+};
+thread_local Attn2Config t_attn2;
 
 bool valid_nkv(int nkv) { return nkv == 1 || nkv == 2 || nkv == 4 || nkv == 8; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -315,9 +323,12 @@ void qkvf_release(void)
     (void)hipGetDevice(&cur);
     for (int d = 0; d < kMaxDevices; ++d) {
         DeviceState &st = g_dev[d];
-        if (st.ws != nullptr) {
+        if (st.ws != nullptr || st.attn2_ws != nullptr) {
             (void)hipSetDevice(d);
-            (void)hipFree(st.ws);
+            if (st.ws != nullptr)
+                (void)hipFree(st.ws);
+            if (st.attn2_ws != nullptr)
+                (void)hipFree(st.attn2_ws);
         }
         st = DeviceState{};
     }
@@ -325,6 +336,85 @@ void qkvf_release(void)
         (void)hipSetDevice(cur);
     t_N = 0;
     t_nkv = 0;
+    t_attn2 = Attn2Config{};
+}
+
+int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int window)
+{
+    if (!valid_nkv(num_kv_heads) || max_model_len < 8 || window < 0)
+        return QKVF_ERR_SHAPE;
+    if (max_reqs < 1 || max_reqs > kAttn2MaxReqs)
+        return QKVF_ERR_ROWS;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    const int ds = current_device(&dev);
+    if (ds != QKVF_OK)
+        return ds;
+    DeviceState &st = g_dev[dev];
+    // A window that covers every position is no window.
+    const int win = window >= max_model_len ? 0 : window;
+    const int z = attn2_splits(num_kv_heads, max_model_len, win);
+    const size_t need = z > 1 ? size_t(max_reqs) * num_kv_heads * z * 64 * kAttn2PartialFloats : 0;
+    if (need > st.attn2_ws_floats) {
+        void *p = nullptr;
+        if (hipMalloc(&p, need * sizeof(float)) != hipSuccess) {
+            (void)hipGetLastError();
+            return QKVF_ERR_ALLOC;
+        }
+        if (st.attn2_ws != nullptr) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(st.attn2_ws);
+        }
+        st.attn2_ws = static_cast<float *>(p);
+        st.attn2_ws_floats = need;
+    }
+    t_attn2 = Attn2Config{num_kv_heads, max_model_len, max_reqs, win, z};
+    return QKVF_OK;
+}
+
+int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate, int64_t gate_row_stride,
+                   const void *kv_cache, const int32_t *block_table, int64_t block_table_stride,
+                   const int32_t *seq_lens, int num_reqs, void *out, int64_t out_row_stride,
+                   hipStream_t stream)
+{
+    const Attn2Config cfg = t_attn2;
+    if (cfg.nkv == 0)
+        return QKVF_ERR_NOT_PREPARED;
+    if (num_reqs < 1 || num_reqs > cfg.max_reqs)
+        return QKVF_ERR_ROWS;
+    if (!q || !gate || !kv_cache || !block_table || !seq_lens || !out)
+        return QKVF_ERR_NULLPTR;
+    const int64_t width = int64_t(kQPerKv) * cfg.nkv * kHeadDim;
+    if (q_row_stride < width || gate_row_stride < width || out_row_stride < width ||
+        block_table_stride < 1)
+        return QKVF_ERR_SHAPE;
+    if (!aligned(q, 16) || q_row_stride % 8 || !aligned(gate, 8) || gate_row_stride % 4 ||
+        !aligned(out, 8) || out_row_stride % 4 || !aligned(kv_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4))
+        return QKVF_ERR_ALIGN;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKVF_ERR_DEVICE;
+    const DeviceState &st = g_dev[dev];
+    const size_t need =
+        cfg.splits > 1 ? size_t(num_reqs) * cfg.nkv * cfg.splits * 64 * kAttn2PartialFloats : 0;
+    if (need > st.attn2_ws_floats)
+        return QKVF_ERR_NOT_PREPARED;
+    const hipError_t e = launch_attn2(q, q_row_stride, gate, gate_row_stride, kv_cache, cfg.nkv,
+                                      block_table, block_table_stride, seq_lens, num_reqs,
+                                      cfg.max_model_len, cfg.window, cfg.splits, st.attn2_ws, out, out_row_stride,
+                                      stream);
+    return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
+}
+
+int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int *splits)
+{
+    if (!valid_nkv(num_kv_heads) || max_model_len < 8 || window < 0)
+        return QKVF_ERR_SHAPE;
+    if (splits)
+        *splits = attn2_splits(num_kv_heads, max_model_len,
+                               window >= max_model_len ? 0 : window);
+    return QKVF_OK;
 }
 
 }  // extern "C"

@@ -61,4 +61,34 @@ hipError_t check_placement(unsigned *scratch, bool *round_robin);
 // (0 on error).  The kernel needs all kGrid blocks resident together.
 int blocks_per_cu(int nkv);
 
+// attn2: softmax scale is 1/sqrt(64) (applied in the kernel), o-norm epsilon.
+constexpr float kAttn2Eps = 1e-6f;
+// A split's partial of one query row: max, sum, 2 words of padding, O[64].
+constexpr int kAttn2PartialFloats = 4 + kHeadDim;
+constexpr int kAttn2MaxReqs = 64;
+
+// Key splits of an attn2 launch: 1 for short contexts (max_model_len <= 2048)
+// and for a window (it spans at most window + 7 keys), else about 256 blocks
+// per request over the KV heads.  Depends on the deployment only.
+inline int attn2_splits(int nkv, int max_model_len, int window)
+{
+    if (window > 0 || max_model_len <= 2048)
+        return 1;
+    int z = 256 / nkv;
+    const int by_len = max_model_len / 512;  // at least 512 keys per split
+    if (z > by_len)
+        z = by_len;
+    if (z > 64)
+        z = 64;
+    return z < 1 ? 1 : z;
+}
+
+// Enqueue attn2 (and its merge when Z > 1) on `stream`; arguments validated
+// by the caller; ws holds R * nkv * Z * 64 * kAttn2PartialFloats floats.
+hipError_t launch_attn2(const void *q, int64_t q_stride, const void *gate, int64_t gate_stride,
+                        const void *kv_cache, int nkv, const int32_t *block_table,
+                        int64_t bt_stride, const int32_t *seq_lens, int R, int max_len,
+                        int window, int Z, float *ws, void *out, int64_t out_stride,
+                        hipStream_t stream);
+
 }  // namespace qkvf

@@ -13,6 +13,19 @@ cute_ops page, split_qkv and the attn2 contract for widths and the cache):
             sin(p * f_i) in column 32 + i, f_i = theta^(-2i/64), theta 10000
             (the interleaved rotary table's usual construction);
   kv_cache  bf16 [pages, nkv, 16, 128] prefilled with random bits.
+
+attn2 (cute_ops page, attn2 contract: 8 query rows per request, any L >= 8,
+head_dim 64, 8 q heads per KV head, an optional window):
+  y         bf16 [8 R, 1152 nkv] ~ N(0, 1), the front's output rows whose q
+            and gate columns attn2 reads (q and k heads come out of the
+            front's norm with RMS 1, and v = x W_v has unit variance for
+            x ~ N(0, 1), W ~ N(0, 0.011^2), K = 8192), optionally q scaled
+            for peakier softmax;
+  kv_cache  bf16 [pages, nkv, 16, 128] ~ N(0, 1);
+  block_table int32 [R, ceil(max_model_len / 16)]: request r owns a random
+            set of distinct pages (disjoint across requests and sets), the
+            unused tail of each row points at page 0;
+  seq_lens  int32 [R], per workload.
 """
 from __future__ import annotations
 
@@ -178,3 +191,124 @@ def describe(w: Workload) -> dict:
 def rope_angle(pos: int, pair: int, theta: float = ROPE_THETA) -> float:
     """The rotation angle the table above encodes for (position, pair)."""
     return pos * math.pow(theta, -2.0 * pair / HEAD_DIM)
+
+
+# ---------------------------------------------------------------- attn2 --
+
+@dataclasses.dataclass(frozen=True)
+class Attn2Workload:
+    name: str
+    nkv: int
+    max_model_len: int
+    lens: tuple            # context length L of each request (>= 8)
+    window: int = 0        # 0: no sliding window
+    sets: int = 1          # request sets on disjoint pages, rotated per call
+    q_scale: float = 1.0
+    index: int = 0
+
+    @property
+    def R(self) -> int:
+        return len(self.lens)
+
+    @property
+    def pages_per_req(self) -> int:
+        return (max(self.lens) + PAGE_SLOTS - 1) // PAGE_SLOTS
+
+    @property
+    def pages(self) -> int:
+        return 1 + self.sets * self.R * self.pages_per_req
+
+    @property
+    def table_width(self) -> int:
+        return (self.max_model_len + PAGE_SLOTS - 1) // PAGE_SLOTS
+
+    @property
+    def eff_window(self) -> int:
+        """The window that matters: none when it covers max_model_len."""
+        return 0 if self.window >= self.max_model_len else self.window
+
+    def first_key(self, L: int) -> int:
+        """Earliest key any of the request's 8 rows attends."""
+        w = self.eff_window
+        return max(0, L - 8 - w + 1) if w > 0 else 0
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes one call must move: q and gate rows read, the output
+        written, the K|V slots of every attended key read once per KV head,
+        the block-table entries of the pages they sit in, and seq_lens."""
+        nq = QHEADS_PER_KV * self.nkv
+        rows = 8 * self.R
+        b = 3 * rows * nq * HEAD_DIM * 2 + 4 * self.R
+        for L in self.lens:
+            lo = self.first_key(L)
+            b += (L - lo) * self.nkv * SLOT_WIDTH * 2
+            b += 4 * ((L + PAGE_SLOTS - 1) // PAGE_SLOTS - lo // PAGE_SLOTS)
+        return b
+
+
+# attn2 workloads: the verify step of one request (8 rows) with the 8 KV
+# heads of the M = 8 front, two requests (M = 16) with mixed lengths, the
+# 2-KV-head draft with a short context, and a sliding-window layer.
+A1 = Attn2Workload("attn2_r1_nkv8_L32768", nkv=8, max_model_len=131072, lens=(32768,),
+                   sets=16, index=11)
+A2 = Attn2Workload("attn2_r2_nkv8_L30000_9001", nkv=8, max_model_len=32768,
+                   lens=(30000, 9001), sets=12, index=12)
+A3 = Attn2Workload("attn2_r1_nkv2_L1500_draft", nkv=2, max_model_len=2048, lens=(1500,),
+                   sets=64, index=13)
+A4 = Attn2Workload("attn2_r2_nkv8_win4096", nkv=8, max_model_len=131072, lens=(20000, 4100),
+                   window=4096, sets=32, index=14)
+A0 = Attn2Workload("attn2_r3_nkv2_small", nkv=2, max_model_len=4096, lens=(300, 41, 8),
+                   q_scale=3.0, index=10)
+ATTN2_WORKLOADS = {a.name: a for a in (A0, A1, A2, A3, A4)}
+
+
+def make_attn2_y(a: Attn2Workload, set_index: int = 0, device="cpu") -> torch.Tensor:
+    """bf16 [8 R, 1152 nkv] rows of the front's output; q columns scaled by
+    q_scale."""
+    g = _gen((1000 * a.index + set_index) * 7919 + 5)
+    y = torch.randn(8 * a.R, n_cols(a.nkv), generator=g, dtype=torch.float32)
+    y[:, :QHEADS_PER_KV * a.nkv * HEAD_DIM] *= a.q_scale
+    return y.to(torch.bfloat16).to(device)
+
+
+def attn2_views(y: torch.Tensor, nkv: int):
+    """(q, gate) column views of the front's output rows: [q | k | v | gate]."""
+    nq = QHEADS_PER_KV * nkv * HEAD_DIM
+    g0 = nq + 2 * nkv * HEAD_DIM
+    return y[:, :nq], y[:, g0:g0 + nq]
+
+
+def make_attn2_cache(a: Attn2Workload, device="cpu") -> torch.Tensor:
+    """bf16 [pages, nkv, 16, 128] ~ N(0, 1); on a device, drawn there."""
+    shape = (a.pages, a.nkv, PAGE_SLOTS, SLOT_WIDTH)
+    if str(device) == "cpu":
+        return torch.randn(shape, generator=_gen(1000 * a.index * 7919 + 6)).to(torch.bfloat16)
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 * a.index * 7919 + 7)
+    c = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    c.normal_(0.0, 1.0, generator=g)
+    return c
+
+
+def make_attn2_table(a: Attn2Workload, set_index: int = 0) -> torch.Tensor:
+    """int32 [R, table_width]: set s, request r owns pages drawn without
+    replacement from its own disjoint block, in random order."""
+    g = _gen(1000 * a.index * 7919 + 8)
+    perm = torch.randperm(a.pages - 1, generator=g) + 1   # page 0 is the filler
+    P = a.pages_per_req
+    bt = torch.zeros(a.R, a.table_width, dtype=torch.int32)
+    for r in range(a.R):
+        start = (set_index * a.R + r) * P
+        bt[r, :P] = perm[start:start + P].to(torch.int32)
+    return bt
+
+
+def make_attn2_lens(a: Attn2Workload) -> torch.Tensor:
+    assert all(8 <= L <= a.max_model_len for L in a.lens)
+    return torch.tensor(a.lens, dtype=torch.int32)
+
+
+def describe_attn2(a: Attn2Workload) -> dict:
+    return {"workload": a.name, "requests": a.R, "query_rows": 8 * a.R, "num_kv_heads": a.nkv,
+            "seq_lens": list(a.lens), "max_model_len": a.max_model_len, "window": a.window,
+            "cache_pages": a.pages}

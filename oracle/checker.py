@@ -24,7 +24,7 @@ import itertools
 
 import numpy as np
 
-from . import (HEAD_DIM, PAGE_SLOTS, QHEADS_PER_KV, bf16_to_float, epilogue,
+from . import (HEAD_DIM, PAGE_SLOTS, QHEADS_PER_KV, attn2, bf16_to_float, epilogue,
                head, n_cols, project, round_projection)
 
 RTOL = 1.6e-2
@@ -171,3 +171,29 @@ def check_front(x, W, positions, slots, cos_sin, nkv: int, eps: float,
         raise ParityError(f"cache differs from the expected placement at "
                           f"{tuple(diff[0])} ({len(diff)} elements)")
     return report
+
+
+def check_attn2(out, q, gate, kv_cache, nkv: int, block_table, seq_lens, window: int = 0):
+    """Compare an attn2 result (uint16 bf16 bits [8 R, >= 512 nkv]) with the
+    oracle on the same inputs, element by element, to RTOL / ATOL.
+
+    The attention output is one fp32-order-dependent real per element before
+    its final bf16 rounding, so a correct result differs from the oracle by
+    its summation error plus at most one bf16 unit (2^-8 relative), both far
+    inside RTOL; no tie enumeration is needed."""
+    ref = attn2(q, gate, kv_cache, nkv, block_table, seq_lens, window)
+    width = QHEADS_PER_KV * nkv * HEAD_DIM
+    got = bf16_to_float(np.ascontiguousarray(out[:, :width]))
+    want = bf16_to_float(ref)
+    ok = _within(got, want)
+    if not ok.all():
+        rows, cols = np.nonzero(~ok)
+        i = int(np.argmax(np.abs(got - want) * ~ok))
+        r, c = divmod(i, width)
+        raise ParityError(
+            f"attn2: {len(rows)} of {got.size} outputs outside tolerance; worst at row {r} "
+            f"(request {r // 8}, token {r % 8}) head {c // HEAD_DIM} dim {c % HEAD_DIM}: "
+            f"gpu {got[r, c]!r} oracle {want[r, c]!r}")
+    err = np.abs(got - want)
+    return {"outputs": int(got.size), "max_abs_err": float(err.max()),
+            "max_err_over_tol": float((err / (RTOL * np.abs(want) + ATOL)).max())}

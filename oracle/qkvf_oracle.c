@@ -231,13 +231,18 @@ void qkvfo_attn2(const uint16_t *q, int64_t q_stride, const uint16_t *gate,
                  double eps, uint16_t *out, int64_t out_stride)
 {
     const int nq = QHEADS_PER_KV * nkv;
-    for (int r = 0; r < R; ++r) {
+    /* (row, head) pairs are independent; threads only share the loop. */
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t idx = 0; idx < (int64_t)R * 8 * nq; ++idx) {
+        const int r = (int)(idx / (8 * nq));
+        const int t = (int)(idx / nq % 8);
+        const int h = (int)(idx % nq);
         const int L = seq_lens[r];
-        for (int t = 0; t < 8; ++t) {
+        {
             const int64_t row = (int64_t)r * 8 + t;
             const int p = L - 8 + t;
             const int lo = window > 0 ? (p - window + 1 > 0 ? p - window + 1 : 0) : 0;
-            for (int h = 0; h < nq; ++h) {
+            {
                 const int j = h / QHEADS_PER_KV;
                 const uint16_t *qh = q + row * q_stride + (int64_t)h * HEAD_DIM;
                 double m = -INFINITY;

@@ -25,7 +25,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qkvf_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qkvf_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_exports():
@@ -133,3 +133,39 @@ def test_no_device_here_means_device_error(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert L.qkvf_prepare(1152, 1, 1) == 1
+
+
+@pytest.mark.parametrize("nkv,mml,window,splits", [
+    (8, 131072, 0, 32), (1, 131072, 0, 64), (2, 4096, 0, 8), (4, 8192, 0, 16),
+    (8, 2048, 0, 1), (8, 2049, 0, 4), (8, 131072, 4096, 1), (2, 2048, 4096, 1),
+    (1, 8, 0, 1),
+])
+def test_attn2_plan(L, nkv, mml, window, splits):
+    """Split count: 1 up to max_model_len 2048 or with a window, else
+    min(256 / nkv, max_model_len / 512, 64)."""
+    import ctypes
+    z = ctypes.c_int(-1)
+    assert L.qkvf_attn2_plan(nkv, mml, window, ctypes.byref(z)) == 0
+    assert z.value == splits
+    assert qf.attn2_plan(nkv, mml, window) == splits
+
+
+@pytest.mark.parametrize("nkv,mml,reqs,window,code", [
+    (3, 4096, 1, 0, 2), (0, 4096, 1, 0, 2), (8, 7, 1, 0, 2), (8, 4096, 1, -1, 2),
+    (8, 4096, 0, 0, 3), (8, 4096, 65, 0, 3),
+])
+def test_attn2_prepare_rejects_bad_shapes_before_the_device(L, nkv, mml, reqs, window, code):
+    assert L.qkvf_attn2_prepare(nkv, mml, reqs, window) == code
+    assert L.qkvf_attn2_plan(nkv, mml, max(window, 0), None) in (0, 2)
+
+
+def test_attn2_run_without_prepare_is_refused(L):
+    res = []
+
+    def fresh_thread():
+        res.append(L.qkvf_attn2_run(16, 4096, 16, 4096, 16, 16, 1, 16, 1, 16, 4096, None))
+
+    t = threading.Thread(target=fresh_thread)
+    t.start()
+    t.join()
+    assert res == [6]
