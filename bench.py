@@ -12,6 +12,7 @@ in HBM.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -62,6 +63,8 @@ def parse():
     ap.add_argument("--repeats", type=int, default=3, help="timed repeats; the median is kept")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and sweep point; one JSON line each on stderr")
+    ap.add_argument("--attn2", default="", metavar="WORKLOAD",
+                    help="time attn2 instead of the front: one of " + ", ".join(wl.ATTN2_WORKLOADS))
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="instead of the front, time device-to-device copies of MB megabytes "
                          "(a plain copy kernel of known size, for scaling memory counters)")
@@ -156,6 +159,112 @@ def time_front(w: wl.Workload, sets: int, steps: int, warmup: int, repeats: int)
     return sorted(times)[len(times) // 2], times
 
 
+class Attn2Pool:
+    """Device-resident inputs of S attn2 calls: request sets on disjoint
+    pages of one cache (so a call's K|V is not left in the MALL by the
+    previous one), each with its own q | gate rows, table and output."""
+
+    def __init__(self, a: wl.Attn2Workload, sets: int):
+        dev = "cuda"
+        self.a = a = dataclasses.replace(a, sets=sets)
+        self.sets = sets
+        self.cache = wl.make_attn2_cache(a, device=dev)
+        self.y = [wl.make_attn2_y(a, s, device=dev) for s in range(sets)]
+        tables = [wl.make_attn2_table(a, s) for s in range(sets)]
+        need = a.pages_per_req
+        for t in tables:   # every page a call can read is inside the cache
+            assert int(t[:, :need].min()) >= 0 and int(t[:, :need].max()) < a.pages
+        self.table = [t.to(dev) for t in tables]
+        self.lens = wl.make_attn2_lens(a).to(dev)
+        width = wl.QHEADS_PER_KV * a.nkv * wl.HEAD_DIM
+        self.out = [torch.empty(8 * a.R, width, dtype=torch.bfloat16, device=dev)
+                    for _ in range(sets)]
+
+    def call(self, i: int, stream) -> None:
+        s = i % self.sets
+        q, g = wl.attn2_views(self.y[s], self.a.nkv)
+        qf.attn2_run(q, g, self.cache, self.table[s], self.lens, self.out[s], stream=stream)
+
+
+def attn2_sets(a: wl.Attn2Workload) -> int:
+    kv = a.algorithmic_bytes()
+    return max(a.sets, int(600e6 // kv) + 1)
+
+
+def time_attn2(a: wl.Attn2Workload, steps: int, warmup: int, repeats: int):
+    sets = attn2_sets(a)
+    pool = Attn2Pool(a, sets)
+    qf.attn2_prepare(a.nkv, a.max_model_len, a.R, a.window)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            pool.call(i, stream)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            pool.call(warmup + i, stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / steps)
+    del pool
+    torch.cuda.empty_cache()
+    return sorted(times)[len(times) // 2], times, sets
+
+
+def attn2_cpu_baseline(a: wl.Attn2Workload, budget_s: float) -> dict | None:
+    """The attn2 oracle on full calls of the same workload (set 0)."""
+    if budget_s <= 0:
+        return None
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    a1 = dataclasses.replace(a, sets=1)
+    y = wl.make_attn2_y(a1, 0)
+    q, g = wl.attn2_views(y, a.nkv)
+    qb, gb = wl.bits(q), wl.bits(g)
+    cache = wl.bits(wl.make_attn2_cache(a1))
+    table = wl.make_attn2_table(a1, 0).numpy()
+    lens = wl.make_attn2_lens(a1).numpy()
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attn2(qb, gb, cache, a.nkv, table, lens, a.eff_window)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (el / calls) * (calls + 1) > 2 * budget_s:
+            break
+    per_call = el / calls
+    return {"value": round(a.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
+            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "kind": "oracle",
+            "sample": f"{calls} full oracle calls of {a.name} (request set 0), "
+                      f"OpenMP over (row, head) pairs, up to {threads} threads"}
+
+
+def attn2_line(a: wl.Attn2Workload, args) -> dict:
+    ms, times, sets = time_attn2(a, args.steps, args.warmup, args.repeats)
+    nbytes = a.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    z = qf.attn2_plan(a.nkv, a.max_model_len, a.window, a.R)
+    kernels = "attn2_split" + (" + attn2_merge" if z > 1 else "")
+    return {
+        "metric": "attn2 achieved HBM GB/s (algorithmic bytes per call / time per call)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(wl.describe_attn2(a), splits=z, request_sets_rotated=sets,
+                       algorithmic_bytes_per_call=nbytes),
+        "roofline": {"bound": "hbm", "kernel": f"{kernels} (the whole call)",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "repeats_ms": [round(t, 6) for t in times],
+    }
+
+
 def rotated_sets(w: wl.Workload, requested: int) -> int:
     sets = requested or w.wsets
     # enough weight sets that the rotation exceeds the 256 MB MALL
@@ -194,6 +303,14 @@ def main():
     if a.copy_calibration > 0:
         copy_calibration(a.copy_calibration, a.steps)
         return
+    if a.attn2:
+        if a.attn2 not in wl.ATTN2_WORKLOADS:
+            raise SystemExit(f"unknown attn2 workload {a.attn2}")
+        aw = wl.ATTN2_WORKLOADS[a.attn2]
+        line = attn2_line(aw, a)
+        line["cpu_baseline"] = attn2_cpu_baseline(aw, a.cpu_baseline_seconds)
+        print(json.dumps(line), flush=True)
+        return
     w = workload_by_name(a.workload)
     sets = rotated_sets(w, a.wsets)
     ms, times = time_front(w, sets, a.steps, a.warmup, a.repeats)
@@ -209,6 +326,15 @@ def main():
                               "us_per_call": round(oms * 1e3, 3), "GB_per_s": round(ogbs, 1),
                               "frac_of_8TBs": round(ogbs / HBM_PEAK_GBS, 4),
                               "weight_sets_rotated": rotated_sets(o, 0)}),
+                  file=sys.stderr, flush=True)
+        for aw in wl.ATTN2_WORKLOADS.values():
+            if aw is wl.A0:   # the small parity case, not a timing workload
+                continue
+            line = attn2_line(aw, a)
+            print(json.dumps({"workload": aw.name, "splits": line["config"]["splits"],
+                              "us_per_call": line["us_per_call"], "GB_per_s": line["value"],
+                              "frac_of_8TBs": line["roofline"]["frac"],
+                              "request_sets_rotated": line["config"]["request_sets_rotated"]}),
                   file=sys.stderr, flush=True)
     base = cpu_baseline(w, a.cpu_baseline_seconds)
     traffic = measured_traffic(w)

@@ -174,8 +174,9 @@ int qkvf_device_fault(void);
  * qkvf_attn2_prepare binds a layer's (num_kv_heads, max_model_len,
  * max_reqs, window) to the calling thread (window 0: none; a window of at
  * least max_model_len is none) and sizes the device workspace in which
- * long-context calls split their keys (the split count depends on these
- * values only, so the launch shape is fixed and capturable).  It may
+ * calls split their keys over several blocks (the split count depends on
+ * these values and the call's request count only, see qkvf_attn2_plan, so
+ * the launch shape of a batch size is fixed and capturable).  It may
  * allocate and synchronize; no attn2 call may be in flight.
  * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS (max_reqs outside [1, 64]),
  * QKVF_ERR_DEVICE, QKVF_ERR_ALLOC.
@@ -209,9 +210,13 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate,
                    const int32_t *seq_lens, int num_reqs, void *out,
                    int64_t out_row_stride, hipStream_t stream);
 
-/* The number of key splits attn2 uses for a layer (a pure function of its
- * arguments).  Returns QKVF_OK or QKVF_ERR_SHAPE. */
-int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int *splits);
+/* The number of key splits attn2 uses for a layer and a request count: about
+ * 512 / (num_reqs * num_kv_heads) blocks per request and KV head, at most
+ * one per 256 keys of the span a request's rows attend (max_model_len, or
+ * window + 7), at most 64; 1 means no merge pass.  A pure function of its
+ * arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or QKVF_ERR_ROWS. */
+int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_reqs,
+                    int *splits);
 
 /* Free the workspace of every device and forget prepared shapes.  No call
  * may be in flight. */

@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
     L.qkvf_attn2_prepare.restype = I
     L.qkvf_attn2_run.argtypes = [P, I64, P, I64, P, P, I64, P, I, P, I64, P]
     L.qkvf_attn2_run.restype = I
-    L.qkvf_attn2_plan.argtypes = [I, I, I, P]
+    L.qkvf_attn2_plan.argtypes = [I, I, I, I, P]
     L.qkvf_attn2_plan.restype = I
     L.qkvf_release.argtypes = []
     L.qkvf_release.restype = None
@@ -177,9 +177,10 @@ def attn2_run(q, gate, kv_cache, block_table, seq_lens, out, stream=None) -> Non
     _raise(st, "qkvf_attn2_run")
 
 
-def attn2_plan(num_kv_heads: int, max_model_len: int, window: int = 0) -> int:
-    """qkvf_attn2_plan: the number of key splits of the layer's launches."""
+def attn2_plan(num_kv_heads: int, max_model_len: int, window: int = 0, num_reqs: int = 1) -> int:
+    """qkvf_attn2_plan: the number of key splits of a launch for num_reqs
+    requests (1: no merge pass)."""
     z = ctypes.c_int()
     _raise(lib().qkvf_attn2_plan(int(num_kv_heads), int(max_model_len), int(window),
-                                 ctypes.byref(z)), "qkvf_attn2_plan")
+                                 int(num_reqs), ctypes.byref(z)), "qkvf_attn2_plan")
     return z.value

@@ -39,7 +39,7 @@ thread_local int t_nkv = 0;
 
 // attn2 configuration bound by the last qkvf_attn2_prepare of this thread.
 struct Attn2Config {
-    int nkv = 0, max_model_len = 0, max_reqs = 0, window = 0, splits = 0;
+    int nkv = 0, max_model_len = 0, max_reqs = 0, window = 0;
 };
 thread_local Attn2Config t_attn2;
 
@@ -353,8 +353,7 @@ int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int wi
     DeviceState &st = g_dev[dev];
     // A window that covers every position is no window.
     const int win = window >= max_model_len ? 0 : window;
-    const int z = attn2_splits(num_kv_heads, max_model_len, win);
-    const size_t need = z > 1 ? size_t(max_reqs) * num_kv_heads * z * 64 * kAttn2PartialFloats : 0;
+    const size_t need = attn2_workspace_floats(num_kv_heads, max_reqs, max_model_len, win);
     if (need > st.attn2_ws_floats) {
         void *p = nullptr;
         if (hipMalloc(&p, need * sizeof(float)) != hipSuccess) {
@@ -368,7 +367,7 @@ int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int wi
         st.attn2_ws = static_cast<float *>(p);
         st.attn2_ws_floats = need;
     }
-    t_attn2 = Attn2Config{num_kv_heads, max_model_len, max_reqs, win, z};
+    t_attn2 = Attn2Config{num_kv_heads, max_model_len, max_reqs, win};
     return QKVF_OK;
 }
 
@@ -396,23 +395,25 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate, int64_
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QKVF_ERR_DEVICE;
     const DeviceState &st = g_dev[dev];
-    const size_t need =
-        cfg.splits > 1 ? size_t(num_reqs) * cfg.nkv * cfg.splits * 64 * kAttn2PartialFloats : 0;
+    const int z = attn2_splits(cfg.nkv, num_reqs, cfg.max_model_len, cfg.window);
+    const size_t need = z > 1 ? size_t(num_reqs) * cfg.nkv * z * 64 * kAttn2PartialFloats : 0;
     if (need > st.attn2_ws_floats)
         return QKVF_ERR_NOT_PREPARED;
     const hipError_t e = launch_attn2(q, q_row_stride, gate, gate_row_stride, kv_cache, cfg.nkv,
                                       block_table, block_table_stride, seq_lens, num_reqs,
-                                      cfg.max_model_len, cfg.window, cfg.splits, st.attn2_ws, out, out_row_stride,
+                                      cfg.max_model_len, cfg.window, z, st.attn2_ws, out, out_row_stride,
                                       stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }
 
-int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int *splits)
+int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_reqs, int *splits)
 {
     if (!valid_nkv(num_kv_heads) || max_model_len < 8 || window < 0)
         return QKVF_ERR_SHAPE;
+    if (num_reqs < 1 || num_reqs > kAttn2MaxReqs)
+        return QKVF_ERR_ROWS;
     if (splits)
-        *splits = attn2_splits(num_kv_heads, max_model_len,
+        *splits = attn2_splits(num_kv_heads, num_reqs, max_model_len,
                                window >= max_model_len ? 0 : window);
     return QKVF_OK;
 }

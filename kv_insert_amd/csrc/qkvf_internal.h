@@ -67,20 +67,47 @@ constexpr float kAttn2Eps = 1e-6f;
 constexpr int kAttn2PartialFloats = 4 + kHeadDim;
 constexpr int kAttn2MaxReqs = 64;
 
-// Key splits of an attn2 launch: 1 for short contexts (max_model_len <= 2048)
-// and for a window (it spans at most window + 7 keys), else about 256 blocks
-// per request over the KV heads.  Depends on the deployment only.
-inline int attn2_splits(int nkv, int max_model_len, int window)
+// Key splits of an attn2 launch.  A request's rows span at most
+// max_model_len keys (window + 7 with a window); the keys are cut into about
+// kAttn2TargetBlocks / (num_reqs * nkv) splits so that a launch has ~512
+// blocks (two per CU), but no split is shorter than kAttn2MinSplitKeys keys
+// (each split writes a 17 KB partial per KV head) and there are at most 64.
+// The count depends on the deployment and the batch size, not on the step's
+// lengths, so the launch shape is fixed for a captured batch size; shorter
+// contexts leave the trailing splits empty.
+constexpr int kAttn2TargetBlocks = 512;
+constexpr int kAttn2MinSplitKeys = 256;
+constexpr int kAttn2MaxSplits = 64;
+
+inline int attn2_span(int max_model_len, int window)
 {
-    if (window > 0 || max_model_len <= 2048)
-        return 1;
-    int z = 256 / nkv;
-    const int by_len = max_model_len / 512;  // at least 512 keys per split
+    return window > 0 && window + 7 < max_model_len ? window + 7 : max_model_len;
+}
+
+inline int attn2_splits(int nkv, int num_reqs, int max_model_len, int window)
+{
+    const int span = attn2_span(max_model_len, window);
+    const int by_len = (span + kAttn2MinSplitKeys - 1) / kAttn2MinSplitKeys;
+    const int per_req = nkv * num_reqs;
+    int z = (kAttn2TargetBlocks + per_req - 1) / per_req;
     if (z > by_len)
         z = by_len;
-    if (z > 64)
-        z = 64;
-    return z < 1 ? 1 : z;
+    if (z > kAttn2MaxSplits)
+        z = kAttn2MaxSplits;
+    return z < 2 ? 1 : z;
+}
+
+// Workspace floats for every batch size up to max_reqs.
+inline size_t attn2_workspace_floats(int nkv, int max_reqs, int max_model_len, int window)
+{
+    size_t most = 0;
+    for (int r = 1; r <= max_reqs; ++r) {
+        const int z = attn2_splits(nkv, r, max_model_len, window);
+        const size_t n = z > 1 ? size_t(r) * nkv * z * 64 * kAttn2PartialFloats : 0;
+        if (n > most)
+            most = n;
+    }
+    return most;
 }
 
 // Enqueue attn2 (and its merge when Z > 1) on `stream`; arguments validated

@@ -89,7 +89,7 @@ def run_attn2(case: Attn2Case, label: str, y=None, cache=None, table=None, lens=
     out = new_out(8 * case.R, 8 * case.nkv * wl.HEAD_DIM) if out is None else out
     say(f"attn2 {label} R={case.R} nkv={case.nkv} lens={list(map(int, ld.cpu()))[:6]} "
         f"mml={case.a.max_model_len} window={case.window} "
-        f"splits={qf.attn2_plan(case.nkv, case.a.max_model_len, case.window)}")
+        f"splits={qf.attn2_plan(case.nkv, case.a.max_model_len, case.window, case.R)}")
     qf.attn2_prepare(case.nkv, case.a.max_model_len, case.R, case.window)
     qf.attn2_run(qd, gd, cd, td, ld, out)
     torch.cuda.synchronize()
@@ -148,8 +148,8 @@ def test_attn2_needles_at_split_and_page_edges():
     a = dataclasses.replace(wl.A1, sets=1)
     case = Attn2Case(a)
     L = a.lens[0]
-    Z = qf.attn2_plan(a.nkv, a.max_model_len, 0)
-    per = (L // 32 + Z - 1) // Z * 32
+    Z = qf.attn2_plan(a.nkv, a.max_model_len, 0, 1)
+    per = max((L // 32 + Z - 1) // Z, 8) * 32
     picks = sorted({0, 1, 15, 16, 31, 32, per - 1, per, per + 1, 2 * per - 1, 2 * per,
                     L - 9, L - 8, L - 2, L - 1})
     cache = case.cache.float()

@@ -135,19 +135,22 @@ def test_no_device_here_means_device_error(L):
     assert L.qkvf_prepare(1152, 1, 1) == 1
 
 
-@pytest.mark.parametrize("nkv,mml,window,splits", [
-    (8, 131072, 0, 32), (1, 131072, 0, 64), (2, 4096, 0, 8), (4, 8192, 0, 16),
-    (8, 2048, 0, 1), (8, 2049, 0, 4), (8, 131072, 4096, 1), (2, 2048, 4096, 1),
-    (1, 8, 0, 1),
+@pytest.mark.parametrize("nkv,mml,window,reqs,splits", [
+    (8, 131072, 0, 1, 64), (8, 32768, 0, 2, 32), (1, 131072, 0, 1, 64), (2, 4096, 0, 1, 16),
+    (4, 8192, 0, 3, 32), (8, 2048, 0, 1, 8), (8, 256, 0, 1, 1), (8, 257, 0, 1, 2),
+    (8, 131072, 4096, 2, 17), (8, 131072, 4096, 1, 17), (2, 2048, 4096, 1, 8),
+    (1, 8, 0, 1, 1), (8, 131072, 0, 64, 1), (8, 131072, 0, 40, 2), (1, 2048, 1, 1, 1),
 ])
-def test_attn2_plan(L, nkv, mml, window, splits):
-    """Split count: 1 up to max_model_len 2048 or with a window, else
-    min(256 / nkv, max_model_len / 512, 64)."""
+def test_attn2_plan(L, nkv, mml, window, reqs, splits):
+    """Split count: ceil(512 / (reqs nkv)) capped by one split per 256 keys of
+    the span (max_model_len, or window + 7) and by 64; 1 below 2."""
     import ctypes
     z = ctypes.c_int(-1)
-    assert L.qkvf_attn2_plan(nkv, mml, window, ctypes.byref(z)) == 0
+    assert L.qkvf_attn2_plan(nkv, mml, window, reqs, ctypes.byref(z)) == 0
     assert z.value == splits
-    assert qf.attn2_plan(nkv, mml, window) == splits
+    assert qf.attn2_plan(nkv, mml, window, reqs) == splits
+    assert L.qkvf_attn2_plan(nkv, mml, window, 0, None) == 3
+    assert L.qkvf_attn2_plan(nkv, mml, window, 65, None) == 3
 
 
 @pytest.mark.parametrize("nkv,mml,reqs,window,code", [
@@ -156,7 +159,7 @@ def test_attn2_plan(L, nkv, mml, window, splits):
 ])
 def test_attn2_prepare_rejects_bad_shapes_before_the_device(L, nkv, mml, reqs, window, code):
     assert L.qkvf_attn2_prepare(nkv, mml, reqs, window) == code
-    assert L.qkvf_attn2_plan(nkv, mml, max(window, 0), None) in (0, 2)
+    assert L.qkvf_attn2_plan(nkv, mml, max(window, 0), 1, None) in (0, 2)
 
 
 def test_attn2_run_without_prepare_is_refused(L):
