@@ -40,21 +40,53 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunk = 32;                     // keys per step (two pages)
-constexpr int kDepth = 4;                      // chunks of loads in flight
-constexpr int kSegPages = 128;                 // pages staged per segment
-constexpr int kSegKeys = kSegPages * kPageSlots;
-constexpr int kMinSplitChunks = kAttn2MinSplitKeys / kChunk;
+#ifndef QKVF_ATTN2_GROUPS
+#define QKVF_ATTN2_GROUPS 4
+#endif
+#ifndef QKVF_ATTN2_DEPTH
+#define QKVF_ATTN2_DEPTH 2
+#endif
+constexpr int kChunk = 32;                     // keys of one MFMA pass (two pages)
+constexpr int kGroups = QKVF_ATTN2_GROUPS;     // key groups (chunks) per step
+constexpr int kStep = kChunk * kGroups;        // keys per step
+constexpr int kThreads = 256 * kGroups;        // 4 query waves per key group
+constexpr int kDepth = QKVF_ATTN2_DEPTH;       // steps of loads in flight
+constexpr int kSegKeys = 2048 / kStep * kStep; // keys per segment: whole steps
+constexpr int kSegPages = kSegKeys / kPageSlots;
+// Splits are whole steps of at least kAttn2MinSplitKeys keys.
+constexpr int kMinSplitChunks = (kAttn2MinSplitKeys / kChunk + kGroups - 1) / kGroups * kGroups;
+static_assert(kGroups >= 1 && kGroups <= 4 && kDepth >= 2 && kDepth % 2 == 0, "launch shape");
+static_assert(kThreads / 8 == kStep, "one thread per 16-byte piece of K and of V");
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.f;           // log2 units the max may lead by
+// Weights are taken relative to a reference point m that trails the true
+// running max by at most this many log2 units, so every weight is <= 2^16.
+constexpr float kRescaleSlack = 16.f;
+constexpr uint32_t kSlackBits = uint32_t(127 + 16) << 23;   // fp32 bits of 2^16
 
 static_assert(kAttn2MaxSplits <= 64, "the merge gives each split one lane");
 
 __device__ inline float sigmoidf(float g) { return 1.f / (1.f + __expf(-g)); }
 
+// LDS layouts of a staged chunk, chosen so that the 16-byte K writes and
+// reads, the 2-byte V^T writes and the 8-byte V^T reads are free of bank
+// conflicts (checked with the LDS bank-conflict counter).
+//  K [32 keys][64 dims]: 16-byte piece p of key k at piece p ^ (k % 8).
+__device__ inline int kswz(int key) { return key & 7; }
+//  V^T [64 dims][32 keys]: row d at row vrow(d); the group of 4 keys
+//  k / 4 at group (k / 4) ^ vgrp(d), with bits d1, d2 ^ d4, d3 ^ d5.
+__device__ inline int vrow(int d) { return d ^ ((d >> 3) & 1); }
+__device__ inline int vgrp(int d)
+{
+    return ((d >> 1) & 1) | ((((d >> 2) ^ (d >> 4)) & 1) << 1) | ((((d >> 3) ^ (d >> 5)) & 1) << 2);
+}
+__device__ inline int vt_index(int d, int key)
+{
+    return vrow(d) * kChunk + ((((key >> 2) ^ vgrp(d)) << 2) | (key & 3));
+}
+
 // How request length L is cut for Z splits: keys from `base` (the page of
-// the earliest attended key) in chunks of 32, `per` chunks per split (at
-// least kMinSplitChunks), `nz` non-empty splits.
+// the earliest attended key) in chunks of 32, `per` chunks per split (whole
+// steps of kGroups chunks, at least kMinSplitChunks), `nz` non-empty splits.
 struct Geom {
     int lo0, base, per, nz;
 };
@@ -66,6 +98,7 @@ __device__ inline Geom split_geom(int L, int window, int Z)
     g.base = g.lo0 & ~(kPageSlots - 1);
     const int chunks = (L - g.base + kChunk - 1) / kChunk;
     g.per = max((chunks + Z - 1) / Z, Z > 1 ? kMinSplitChunks : chunks);
+    g.per = (g.per + kGroups - 1) / kGroups * kGroups;
     g.nz = (chunks + g.per - 1) / g.per;
     return g;
 }
@@ -86,22 +119,26 @@ __device__ inline float wave_sum(float v)
     return v;
 }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kThreads)
 attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__restrict__ gate,
             int64_t gate_stride, const __bf16 *__restrict__ kv_cache, int nkv,
             const int32_t *__restrict__ block_table, int64_t bt_stride,
             const int32_t *__restrict__ seq_lens, int max_len, int window, int Z,
             float *__restrict__ ws, __bf16 *__restrict__ out, int64_t out_stride)
 {
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][kChunk * kHeadDim];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][kHeadDim * kChunk];
+    // Two step buffers of K [128 keys][64] and V^T [4 groups][64][32 keys];
+    // after the key loop the same bytes hold the groups' O for the merge.
+    __shared__ __attribute__((aligned(16))) __bf16 stage_lds[2][2 * kStep * kHeadDim];
     __shared__ int64_t pg[kSegPages];   // element offset of each page's K|V rows
+    __shared__ float2 ml_lds[kGroups][64];
 
     const int z = blockIdx.x, j = blockIdx.y, r = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int grp = tid >> 8;                  // key group: keys 32 grp .. of a step
+    const int wq = (tid >> 6) & 3;             // query wave within the group
     const int c = lane & 15;   // query row of the wave (B column / output column)
-    const int g = lane >> 4;   // lane group: which keys / dims of a step
-    const int hh = 2 * wave + (c >> 3);       // q head within the KV group
+    const int g = lane >> 4;   // lane group: which keys / dims of a chunk
+    const int hh = 2 * wq + (c >> 3);          // q head within the KV group
     const int t = c & 7;                       // token of the row
     const int head = kQPerKv * j + hh;         // q head index in the row
     const int64_t row = int64_t(r) * 8 + t;
@@ -124,16 +161,22 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
     const bf16x8 qv0 = *reinterpret_cast<const bf16x8 *>(qrow + 8 * g);
     const bf16x8 qv1 = *reinterpret_cast<const bf16x8 *>(qrow + 32 + 8 * g);
 
-    float m = -INFINITY;   // running max of this lane's query (log2 units)
-    float l = 0.f;         // this lane's part of the running sum
+    float m = -INFINITY;   // reference point of this lane's query (log2 units)
     f32x4 o[4] = {};       // O^T[16 dt + 4 g + v][c]
-    int buf = 0;
+    f32x4 ls = {};         // running sum of the query's weights (all 4 equal)
+    // A operand of all ones: its product with P^T sums the weights per query
+    // on the matrix core, from the same hi + lo parts as the products with V.
+    const bf16x8 ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                         __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
 
-    // Chunk layout: thread tid moves slot kl = tid / 8 of the chunk's 32
-    // keys, 16-byte part p = tid % 8 of its K (dims 8 p ..) and of its V.
+    // Step layout: thread tid moves slot kl = tid / 8 of the step's 128 keys,
+    // 16-byte part p = tid % 8 of its K (dims 8 p ..) and of its V: K rows of
+    // all 128 keys, then one V^T block per group (layouts above).
     const int kl = tid >> 3, part = tid & 7;
-    const int k_lds = kl * kHeadDim + 8 * (part ^ (kl & 7));   // K swizzle
-    const int v_lds = 8 * part * kChunk + (kl ^ (4 * part));    // V^T swizzle
+    const int k_lds = kl * kHeadDim + 8 * (part ^ kswz(kl));
+    const int v_lds = kStep * kHeadDim + (kl >> 5) * (kHeadDim * kChunk);
+    const int kg_lds = kChunk * grp * kHeadDim;                          // group's K rows
+    const int vg_lds = kStep * kHeadDim + grp * (kHeadDim * kChunk);     // group's V^T
     const __bf16 *kv_head = kv_cache + int64_t(j) * kPageSlots * kSlotWidth + part * 8;
     const int64_t page_elems = int64_t(nkv) * kPageSlots * kSlotWidth;
 
@@ -142,7 +185,7 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
         const int page0 = seg / kPageSlots;
         const int npg = (seg_end - 1) / kPageSlots - page0 + 1;
         const int klo = max(seg, geo.lo0), khi = seg_end;   // keys loaded
-        const int nch = (seg_end - seg + kChunk - 1) / kChunk;
+        const int nst = (seg_end - seg + kStep - 1) / kStep;
         __syncthreads();   // the previous segment is done with pg
         if (tid < npg)
             pg[tid] = block_table[int64_t(r) * bt_stride + page0 + tid] * page_elems;
@@ -150,7 +193,7 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
 
         // Loads are issued unconditionally, so that the number of loads behind
         // each ring slot is the same on every path and the wait before staging
-        // a slot leaves the later slots in flight; a chunk past the segment
+        // a slot leaves the later slots in flight; a step past the segment
         // (never staged) reads the block's own q row, already in cache.  A key
         // outside [klo, khi) loads a valid key and is zeroed at staging.
         auto issue = [&](int k0, bool real, bf16x8 *ring) {
@@ -163,77 +206,87 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
         };
         auto stage = [&](int k0, int sb, const bf16x8 *ring) {
             bf16x8 kp = ring[0], vp = ring[1];
-            if (k0 < klo || k0 + kChunk > khi) {   // edge chunk (uniform)
+            if (k0 < klo || k0 + kStep > khi) {   // edge step (uniform)
                 const bool ok = k0 + kl >= klo && k0 + kl < khi;
                 kp = ok ? kp : bf16x8{};
                 vp = ok ? vp : bf16x8{};
             }
-            *reinterpret_cast<bf16x8 *>(&Ks[sb][k_lds]) = kp;
+            *reinterpret_cast<bf16x8 *>(&stage_lds[sb][k_lds]) = kp;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                Vt[sb][v_lds + e * kChunk] = vp[e];
+                stage_lds[sb][v_lds + vt_index(8 * part + e, kl & 31)] = vp[e];
         };
 
-        // One chunk from LDS buffer `buf`: scores, online softmax, products.
-        auto compute = [&](int k0) {
+        // The group's 32 keys of a step from buffer `buf` (a constant at every
+        // call): scores, online softmax, products.
+        auto compute = [&](int k0, int buf) {
+            const __bf16 *Ks = &stage_lds[buf][kg_lds];
+            const __bf16 *Vt = &stage_lds[buf][vg_lds];
             // S^T for 32 keys: two key tiles of 16 (A row = lane % 16).
             f32x4 s[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 const int key = 16 * kt + c;
                 const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                    &Ks[buf][key * kHeadDim + 8 * (g ^ (key & 7))]);
+                    &Ks[key * kHeadDim + 8 * (g ^ kswz(key))]);
                 const bf16x8 kb = *reinterpret_cast<const bf16x8 *>(
-                    &Ks[buf][key * kHeadDim + 8 * ((4 + g) ^ (key & 7))]);
+                    &Ks[key * kHeadDim + 8 * ((4 + g) ^ kswz(key))]);
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
                 a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv0, a, 0, 0, 0);
                 a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qv1, a, 0, 0, 0);
                 s[kt] = a;
             }
-            // Lane holds raw scores of keys k0 + 16 kt + 4 g + v for query c.
+            // Lane holds raw scores of keys kc + 16 kt + 4 g + v for query c.
             // Only chunks before the last row's window start or past the first
-            // row's position need the mask (a uniform test).
-            if (k0 < lo_last || k0 + kChunk > L - 7) {
+            // row's position need the mask (uniform over the group's waves).
+            const int kc = k0 + kChunk * grp;
+            if (kc < lo_last || kc + kChunk > L - 7) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int kp = k0 + 16 * kt + 4 * g + v;
+                        const int kp = kc + 16 * kt + 4 * g + v;
                         s[kt][v] = kp >= lo && kp <= pos ? s[kt][v] : -INFINITY;
                     }
             }
-            // The reference point m moves only when a scaled score exceeds it
-            // by more than 2^8, so the weights stay <= 256 and the state is
-            // rescaled rarely.  Each lane tests its own 8 keys; only when some
-            // lane of the wave needs more (a wave-uniform branch) are the
-            // query's 4 lane groups reduced to the new reference.
-            const float mo = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            if (__builtin_amdgcn_ballot_w64(mo * sc > m + kRescaleSlack)) {
-                float mc = fmaxf(mo, __shfl_xor(mo, 16, 64));
+            // Weights relative to the reference point: 2^(scale s - m).  The
+            // reference moves only when a weight would exceed 2^16 (tested on
+            // the weights' exponent bits) or nothing has been seen yet; then
+            // (a wave-uniform branch, rare) the query's 4 lane groups are
+            // reduced to its exact running max, the state is rescaled and the
+            // weights are taken again.
+            float e[8];
+            auto weights = [&](float nm) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        e[4 * kt + v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], sc, nm));
+            };
+            weights(m == -INFINITY ? 0.f : -m);
+            uint32_t eb = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                eb = max(eb, __float_as_uint(e[i]));   // weights are >= 0
+            if (__builtin_amdgcn_ballot_w64(m == -INFINITY || eb > kSlackBits)) {
+                float mc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
                 mc = fmaxf(mc, __shfl_xor(mc, 32, 64)) * sc;   // scale > 0 keeps the max
-                const float mn = mc > m + kRescaleSlack ? mc : m;
+                const float mn = m == -INFINITY || mc > m + kRescaleSlack ? mc : m;
                 const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-                l *= alpha;
+                ls *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
                     o[dt] *= alpha;
                 m = mn;
+                // With nothing seen yet (m = -inf) every score here is -inf too.
+                weights(m == -INFINITY ? 0.f : -m);
             }
-            // With nothing seen yet (m = -inf) every score here is -inf too.
-            const float nm = m == -INFINITY ? 0.f : -m;
             // Each weight goes in as bf16 hi + lo parts (two products), so the
             // weights keep about 16 bits rather than bf16's 8: hi is the weight
             // truncated to bf16 (its upper 16 bits, exact), lo = weight - hi
             // (exact in fp32) rounded to bf16.
-            float e[8];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    e[4 * kt + v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], sc, nm));
-                    l += e[4 * kt + v];
-                }
             uint32_t hw[4];
             bf16x8 pl;
 #pragma unroll
@@ -247,88 +300,106 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 // V^T row 16 dt + c (A row = lane % 16): keys 4 g .. and
-                // 16 + 4 g .., stored at key group ^ (row / 8).
+                // 16 + 4 g .. (4 consecutive keys stay together).
                 const int d = 16 * dt + c;
-                const int h = d >> 3;
-                const bf16x4 va = *reinterpret_cast<const bf16x4 *>(
-                    &Vt[buf][d * kChunk + 4 * (g ^ h)]);
-                const bf16x4 vb = *reinterpret_cast<const bf16x4 *>(
-                    &Vt[buf][d * kChunk + 4 * ((4 + g) ^ h)]);
+                const bf16x4 va = *reinterpret_cast<const bf16x4 *>(&Vt[vt_index(d, 4 * g)]);
+                const bf16x4 vb = *reinterpret_cast<const bf16x4 *>(&Vt[vt_index(d, 16 + 4 * g)]);
                 const bf16x8 vv = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, ph, o[dt], 0, 0, 0);
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pl, o[dt], 0, 0, 0);
             }
+            ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph, ls, 0, 0, 0);
+            ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl, ls, 0, 0, 0);
         };
 
         bf16x8 ring[kDepth][2];
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
-            issue(seg + d * kChunk, d < nch, ring[d]);
-        // Full rounds of kDepth chunks keep every ring slot in one place (no
-        // early exit), then the last nch % kDepth chunks.
-        const int full = nch / kDepth * kDepth;
-        for (int c0 = 0; c0 < full; c0 += kDepth) {
+            issue(seg + d * kStep, d < nst, ring[d]);
+        // Full rounds of kDepth steps keep every ring slot in one place (no
+        // early exit), then the last nst % kDepth steps.
+        // Step s of the segment uses buffer s % 2 (kDepth is even, and the
+        // segment's first barrier leaves both buffers free).
+        static_assert(kDepth % 2 == 0, "ring slot d stages into buffer d % 2");
+        const int full = nst / kDepth * kDepth;
+        for (int s0 = 0; s0 < full; s0 += kDepth) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d) {
-                const int k0 = seg + (c0 + d) * kChunk;
-                stage(k0, buf, ring[d]);
-                issue(k0 + kDepth * kChunk, c0 + d + kDepth < nch, ring[d]);
+                const int k0 = seg + (s0 + d) * kStep;
+                stage(k0, d & 1, ring[d]);
+                issue(k0 + kDepth * kStep, s0 + d + kDepth < nst, ring[d]);
                 __syncthreads();
-                compute(k0);
-                buf ^= 1;   // the next chunk stages into the other buffer
+                compute(k0, d & 1);
             }
         }
 #pragma unroll
         for (int d = 0; d < kDepth - 1; ++d) {
-            if (full + d < nch) {
-                const int k0 = seg + (full + d) * kChunk;
-                stage(k0, buf, ring[d]);
+            if (full + d < nst) {
+                const int k0 = seg + (full + d) * kStep;
+                stage(k0, d & 1, ring[d]);
                 __syncthreads();
-                compute(k0);
-                buf ^= 1;
+                compute(k0, d & 1);
             }
         }
     }
 
-    // Totals of the query across its 4 lane groups.
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    // Lane (c, g) holds O^T[16 dt + 4 g + v][c]: dims 16 dt + 4 g + v.
+    // The key groups' states through LDS: group grp's O^T tile of query
+    // q = 8 hh + t goes to red[grp][q][dim] (fp32, the staging bytes), its
+    // (m, l) to ml_lds.
+    const float l = ls[0];
+    float *red = reinterpret_cast<float *>(&stage_lds[0][0]);
+    // (The 16-byte column c4 of row q sits at column c4 ^ (q % 16), so that
+    // the 16 rows a wave writes at once fall in distinct banks.)
+    const int qi = 8 * hh + t;
+    __syncthreads();   // every wave is done with the staging buffers
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+        *reinterpret_cast<f32x4 *>(
+            &red[(grp * 64 + qi) * kHeadDim + 4 * ((4 * dt + g) ^ (qi & 15))]) = o[dt];
+    if (g == 0)
+        ml_lds[grp][qi] = make_float2(m, l);
+    __syncthreads();
+
+    // Thread tid combines query tid / 16, dims 4 (tid % 16) .. + 3.
+    const int cq = tid >> 4, d0 = 4 * (tid & 15);
+    float mg[kGroups], M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kGroups; ++k) {
+        mg[k] = ml_lds[k][cq].x;
+        M = fmaxf(M, mg[k]);
+    }
+    float lt = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kGroups; ++k) {
+        const float w = mg[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg[k] - M);
+        lt += w * ml_lds[k][cq].y;
+        acc += w * *reinterpret_cast<const f32x4 *>(
+                       &red[(k * 64 + cq) * kHeadDim + 4 * ((d0 >> 2) ^ (cq & 15))]);
+    }
+    const int ct = cq & 7, chh = cq >> 3;      // token and q head of query cq
+    const int64_t crow = int64_t(r) * 8 + ct;
+    const int64_t ccol = int64_t(kQPerKv * j + chh) * kHeadDim + d0;
     if (Z == 1) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        float ss = 0.f;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        acc *= inv;
+        float ss = acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                o[dt][v] *= inv;
-                ss += o[dt][v] * o[dt][v];
-            }
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
+        for (int k = 1; k < 16; k <<= 1)
+            ss += __shfl_xor(ss, k, 64);
         const float rr = rsqrtf(ss * (1.f / kHeadDim) + kAttn2Eps);
-        const __bf16 *grow = gate + row * gate_stride + int64_t(head) * kHeadDim;
-        __bf16 *orow = out + row * out_stride + int64_t(head) * kHeadDim;
+        const bf16x4 gv = *reinterpret_cast<const bf16x4 *>(gate + crow * gate_stride + ccol);
+        bf16x4 res;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const int d0 = 16 * dt + 4 * g;
-            const bf16x4 gv = *reinterpret_cast<const bf16x4 *>(grow + d0);
-            bf16x4 res;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                res[v] = __bf16(o[dt][v] * rr * sigmoidf(float(gv[v])));
-            *reinterpret_cast<bf16x4 *>(orow + d0) = res;
-        }
+        for (int v = 0; v < 4; ++v)
+            res[v] = __bf16(acc[v] * rr * sigmoidf(float(gv[v])));
+        *reinterpret_cast<bf16x4 *>(out + crow * out_stride + ccol) = res;
     } else {
-        // Partial of (request, KV head, split, row 8 hh + t): max, sum, O[64].
-        float *dst = ws + (((int64_t(r) * nkv + j) * Z + z) * 64 + 8 * hh + t) * kAttn2PartialFloats;
-        if (g == 0) {
-            dst[0] = m;
-            dst[1] = l;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            *reinterpret_cast<f32x4 *>(dst + 4 + 16 * dt + 4 * g) = o[dt];  // 16-byte aligned
+        // Partial of (request, KV head, split, query cq): max, sum, O[64].
+        float *dst = ws + (((int64_t(r) * nkv + j) * Z + z) * 64 + cq) * kAttn2PartialFloats;
+        if ((tid & 15) == 0)
+            *reinterpret_cast<float2 *>(dst) = make_float2(M, lt);
+        *reinterpret_cast<f32x4 *>(dst + 4 + d0) = acc;   // 16-byte aligned
     }
 }
 
@@ -382,7 +453,7 @@ hipError_t launch_attn2(const void *q, int64_t q_stride, const void *gate, int64
                         int window, int Z, float *ws, void *out, int64_t out_stride,
                         hipStream_t stream)
 {
-    hipLaunchKernelGGL(attn2_split, dim3(Z, nkv, R), dim3(256), 0, stream,
+    hipLaunchKernelGGL(attn2_split, dim3(Z, nkv, R), dim3(kThreads), 0, stream,
                        static_cast<const __bf16 *>(q), q_stride, static_cast<const __bf16 *>(gate),
                        gate_stride, static_cast<const __bf16 *>(kv_cache), nkv, block_table,
                        bt_stride, seq_lens, max_len, window, Z, ws, static_cast<__bf16 *>(out),

@@ -69,13 +69,14 @@ constexpr int kAttn2MaxReqs = 64;
 
 // Key splits of an attn2 launch.  A request's rows span at most
 // max_model_len keys (window + 7 with a window); the keys are cut into about
-// kAttn2TargetBlocks / (num_reqs * nkv) splits so that a launch has ~512
-// blocks (two per CU), but no split is shorter than kAttn2MinSplitKeys keys
+// kAttn2TargetBlocks / (num_reqs * nkv) splits so that a launch has ~256
+// blocks (one 16-wave block per CU), but no split is shorter than
+// kAttn2MinSplitKeys keys
 // (each split writes a 17 KB partial per KV head) and there are at most 64.
 // The count depends on the deployment and the batch size, not on the step's
 // lengths, so the launch shape is fixed for a captured batch size; shorter
 // contexts leave the trailing splits empty.
-constexpr int kAttn2TargetBlocks = 512;
+constexpr int kAttn2TargetBlocks = 256;
 constexpr int kAttn2MinSplitKeys = 256;
 constexpr int kAttn2MaxSplits = 64;
 

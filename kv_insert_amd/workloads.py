@@ -247,8 +247,9 @@ class Attn2Workload:
 
 
 # attn2 workloads: the verify step of one request (8 rows) with the 8 KV
-# heads of the M = 8 front, two requests (M = 16) with mixed lengths, the
-# 2-KV-head draft with a short context, and a sliding-window layer.
+# heads of the M = 8 front at 32K and at the full 128K context, two requests
+# (M = 16) with mixed lengths, the 2-KV-head draft with a short context, and
+# a sliding-window layer.
 A1 = Attn2Workload("attn2_r1_nkv8_L32768", nkv=8, max_model_len=131072, lens=(32768,),
                    sets=16, index=11)
 A2 = Attn2Workload("attn2_r2_nkv8_L30000_9001", nkv=8, max_model_len=32768,
@@ -257,9 +258,11 @@ A3 = Attn2Workload("attn2_r1_nkv2_L1500_draft", nkv=2, max_model_len=2048, lens=
                    sets=64, index=13)
 A4 = Attn2Workload("attn2_r2_nkv8_win4096", nkv=8, max_model_len=131072, lens=(20000, 4100),
                    window=4096, sets=32, index=14)
+A5 = Attn2Workload("attn2_r1_nkv8_L131072", nkv=8, max_model_len=131072, lens=(131072,),
+                   sets=3, index=15)
 A0 = Attn2Workload("attn2_r3_nkv2_small", nkv=2, max_model_len=4096, lens=(300, 41, 8),
                    q_scale=3.0, index=10)
-ATTN2_WORKLOADS = {a.name: a for a in (A0, A1, A2, A3, A4)}
+ATTN2_WORKLOADS = {a.name: a for a in (A0, A1, A2, A3, A4, A5)}
 
 
 def make_attn2_y(a: Attn2Workload, set_index: int = 0, device="cpu") -> torch.Tensor:
