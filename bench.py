@@ -33,21 +33,27 @@ KERNEL_SRC = os.path.join(ROOT, "kv_insert_amd", "csrc", "qkvf_kernels.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "front_fused_counters.json")
 
 
-def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+ATTN2_SRC = os.path.join(ROOT, "kv_insert_amd", "csrc", "qkvf_attn2.hip")
+ATTN2_COUNTERS = os.path.join(ROOT, "profiles", "attn2_counters.json")
 
 
-def measured_traffic(w) -> float | None:
-    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+def kernel_hash(path: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(w, counters: str = COUNTERS, src: str = KERNEL_SRC) -> float | None:
+    """HBM bytes per call from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     recorded in profiles/, if they were taken on the kernel as it is now."""
     try:
-        rec = json.load(open(COUNTERS))
+        rec = json.load(open(counters))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha256_16") != kernel_hash():
+    if rec.get("kernel_sha256_16") != kernel_hash(src):
         return None
     entry = rec.get("workloads", {}).get(w.name)
-    return None if entry is None else entry.get("hbm_bytes_per_launch")
+    if entry is None:
+        return None
+    return entry.get("hbm_bytes_per_launch", entry.get("hbm_bytes_per_call"))
 
 
 def parse():
@@ -260,7 +266,8 @@ def attn2_line(a: wl.Attn2Workload, args) -> dict:
                        algorithmic_bytes_per_call=nbytes),
         "roofline": {"bound": "hbm", "kernel": f"{kernels} (the whole call)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(a, ATTN2_COUNTERS, ATTN2_SRC)},
         "repeats_ms": [round(t, 6) for t in times],
     }
 
