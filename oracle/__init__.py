@@ -73,6 +73,8 @@ def _load():
     lib.qkvfo_front.restype = None
     lib.qkvfo_front.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_double, P, P, P, P, ctypes.c_int]
+    lib.qkvfo_layer_front.restype = None
+    lib.qkvfo_layer_front.argtypes = [P, ctypes.c_int, ctypes.c_int64, P, ctypes.c_double, P, P, P]
     lib.qkvfo_attn2.restype = None
     lib.qkvfo_attn2.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int,
                                 P, ctypes.c_int64, P, ctypes.c_int, ctypes.c_int,
@@ -215,3 +217,31 @@ def attn2(q, gate, kv_cache, nkv: int, block_table, seq_lens, window: int = 0,
                     _ptr(bt), bt.shape[1], _ptr(sl), R, int(window), scale, eps,
                     _ptr(out), out.shape[1])
     return out
+
+
+LAYER_FRONT_EPS = 1e-6   # reading: the pre-QKV-projection norm's epsilon
+
+
+def layer_front(x, weight=None, eps: float = LAYER_FRONT_EPS, aux: bool = False):
+    """LayerFront of rows of 8192: x is uint16 bf16 bits or float32, shape
+    [rows, 8192]; weight uint16 bf16 bits [8192] or None (a weightless norm).
+    Returns (stream fp32, aux fp32 or None, out uint16 bf16 bits)."""
+    lib = _load()
+    x = np.asarray(x)
+    if x.dtype == np.float32:
+        is_fp32 = 1
+    elif x.dtype == np.uint16:
+        is_fp32 = 0
+    else:
+        raise TypeError("x must hold bf16 bits (uint16) or float32")
+    x = np.ascontiguousarray(x)
+    assert x.ndim == 2 and x.shape[1] == HIDDEN
+    rows = x.shape[0]
+    w = None if weight is None else np.ascontiguousarray(weight, dtype=np.uint16)
+    assert w is None or w.shape == (HIDDEN,)
+    stream = np.empty((rows, HIDDEN), np.float32)
+    a = np.empty((rows, HIDDEN), np.float32) if aux else None
+    out = np.empty((rows, HIDDEN), np.uint16)
+    lib.qkvfo_layer_front(_ptr(x), is_fp32, rows, _ptr(w), float(eps), _ptr(stream), _ptr(a),
+                          _ptr(out))
+    return stream, a, out

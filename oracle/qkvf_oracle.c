@@ -24,7 +24,9 @@
  * norm and the rotation are computed in double and rounded once to bf16.
  * Readings where the pages are silent (the norm's form and epsilon, the
  * cos|sin column layout, negative slots) are listed in the header of each
- * function below.
+ * function below.  The file also holds the oracles of the next steps built
+ * on the same pages: attn2 (the verify step's paged attention) and
+ * LayerFront (the row norm that produces x).
  */
 #include <math.h>
 #include <stdint.h>
@@ -284,6 +286,42 @@ void qkvfo_attn2(const uint16_t *q, int64_t q_stride, const uint16_t *gate,
                     dst[d] = qkvfo_double_to_bf16(o[d] * rr * sg);
                 }
             }
+        }
+    }
+}
+
+/*
+ * LayerFront (layer_front page, class LayerFront and its run method): the
+ * first decoder layer's input.  For each of `rows` rows of H = 8192 values:
+ *     stream = float(x)                (x bf16 or fp32; exact)
+ *     aux    = stream                  (only when aux is not NULL)
+ *     out    = bf16(stream * r * w),   r = 1 / sqrt(mean(stream^2) + eps)
+ * where the norm is the layer's pre-QKV-projection RMS norm.  Readings (the
+ * page names the norm but prints neither its form nor its epsilon): the
+ * usual RMS norm over the row with eps inside the root; w is the norm's
+ * bf16 weight, or 1 when the norm has none (weight == NULL); the product is
+ * rounded once, double -> binary32 -> bf16 as for every other output.
+ * x_is_fp32 selects the input type (bf16 bits or fp32 values).
+ */
+void qkvfo_layer_front(const void *x, int x_is_fp32, int64_t rows, const uint16_t *weight,
+                       double eps, float *stream, float *aux, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float s[HIDDEN];
+        for (int k = 0; k < HIDDEN; ++k)
+            s[k] = x_is_fp32 ? ((const float *)x)[r * HIDDEN + k]
+                             : (float)qkvfo_bf16_to_double(((const uint16_t *)x)[r * HIDDEN + k]);
+        double ss = 0.0;
+        for (int k = 0; k < HIDDEN; ++k)
+            ss += (double)s[k] * (double)s[k];
+        const double rr = 1.0 / sqrt(ss / HIDDEN + eps);
+        for (int k = 0; k < HIDDEN; ++k) {
+            stream[r * HIDDEN + k] = s[k];
+            if (aux)
+                aux[r * HIDDEN + k] = s[k];
+            const double w = weight ? qkvfo_bf16_to_double(weight[k]) : 1.0;
+            out[r * HIDDEN + k] = qkvfo_double_to_bf16((double)s[k] * rr * w);
         }
     }
 }
