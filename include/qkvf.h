@@ -56,6 +56,9 @@ typedef enum {
     QKVF_ERR_TIMEOUT = 12       /* qkvf_device_fault: a call gave up waiting for a partial result */
 } qkvf_status;
 
+/* Element types of an input that may come in either (qkvf_layer_front). */
+typedef enum { QKVF_DTYPE_BF16 = 0, QKVF_DTYPE_F32 = 1 } qkvf_dtype;
+
 /*
  * Prepare the front for N output columns, num_kv_heads KV heads and every
  * row count 1..M on the current device (qkv_front page, function "prepare":
@@ -217,6 +220,31 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate,
  * arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or QKVF_ERR_ROWS. */
 int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_reqs,
                     int *splits);
+
+/*
+ * LayerFront: the first decoder layer's input (layer_front page, class
+ * LayerFront, method run).  For each of `rows` rows of 8192 values:
+ *     stream = float(x)                    the fp32 residual stream
+ *     aux    = stream                      only when aux != NULL (an aux layer)
+ *     out    = bf16(stream * r * w),       r = 1 / sqrt(mean(stream^2) + eps)
+ * the layer's pre-QKV-projection RMS norm, whose output is the front's x.
+ * w is the norm's bf16 weight [8192], or 1 when weight == NULL (a weightless
+ * norm).  eps is the norm's epsilon (>= 0, finite).  Device pointers:
+ *   x       [rows][8192] of x_dtype (QKVF_DTYPE_BF16 or QKVF_DTYPE_F32),
+ *           16-byte (bf16) or 32-byte (fp32) aligned, contiguous rows;
+ *   stream  fp32 [rows][8192], 32-byte aligned, written; with an fp32 x it
+ *           may be x itself (updated in place);
+ *   aux     fp32 [rows][8192], 32-byte aligned, written, or NULL;
+ *   out     bf16 [rows][8192], 16-byte aligned, written;
+ *   weight  bf16 [8192], 16-byte aligned, or NULL.
+ * Apart from stream == x, outputs must not overlap each other or the inputs.
+ * rows == 0 does nothing.  One launch on `hip_stream`; allocates nothing and
+ * never synchronizes (graph-capturable).  Errors: QKVF_ERR_SHAPE (x_dtype or
+ * eps), QKVF_ERR_ROWS (rows < 0 or > 2^20), QKVF_ERR_NULLPTR, QKVF_ERR_ALIGN,
+ * QKVF_ERR_DEVICE (not a gfx950), QKVF_ERR_HIP.
+ */
+int qkvf_layer_front(const void *x, int x_dtype, int64_t rows, const void *weight, float eps,
+                     float *stream, float *aux, void *out, hipStream_t hip_stream);
 
 /* Free the workspace of every device and forget prepared shapes.  No call
  * may be in flight. */

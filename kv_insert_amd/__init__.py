@@ -28,7 +28,7 @@ STATUS = {
 }
 EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
            "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_device_fault", "qkvf_release",
-           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan")
+           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front")
 
 
 class QkvfError(ValueError):
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.qkvf_attn2_run.restype = I
     L.qkvf_attn2_plan.argtypes = [I, I, I, I, P]
     L.qkvf_attn2_plan.restype = I
+    L.qkvf_layer_front.argtypes = [P, I, I64, P, ctypes.c_float, P, P, P, P]
+    L.qkvf_layer_front.restype = I
     L.qkvf_release.argtypes = []
     L.qkvf_release.restype = None
     _lib = L
@@ -184,3 +186,23 @@ def attn2_plan(num_kv_heads: int, max_model_len: int, window: int = 0, num_reqs:
     _raise(lib().qkvf_attn2_plan(int(num_kv_heads), int(max_model_len), int(window),
                                  int(num_reqs), ctypes.byref(z)), "qkvf_attn2_plan")
     return z.value
+
+
+DTYPE_BF16, DTYPE_F32 = 0, 1
+
+
+def layer_front(x, stream_out, out, aux=None, weight=None, eps: float = 1e-6, stream=None) -> None:
+    """qkvf_layer_front on torch tensors: x [rows, 8192] bf16 or fp32,
+    stream_out fp32 [rows, 8192] (may be x when x is fp32), out bf16, aux fp32
+    or None, weight bf16 [8192] or None; enqueued on `stream` (a torch or HIP
+    stream, default the current one)."""
+    import torch
+    if x.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        dt = DTYPE_F32
+    else:
+        raise ValueError("x must be bfloat16 or float32")
+    st = lib().qkvf_layer_front(_ptr(x), dt, int(x.shape[0]), _ptr(weight), float(eps),
+                                _ptr(stream_out), _ptr(aux), _ptr(out), _stream_handle(stream))
+    _raise(st, "qkvf_layer_front")

@@ -6,6 +6,7 @@
 #include "qkvf.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -42,6 +43,9 @@ struct Attn2Config {
     int nkv = 0, max_model_len = 0, max_reqs = 0, window = 0;
 };
 thread_local Attn2Config t_attn2;
+
+// The device this thread last checked for qkvf_layer_front (-1: none).
+thread_local int t_lf_dev = -1;
 
 bool valid_nkv(int nkv) { return nkv == 1 || nkv == 2 || nkv == 4 || nkv == 8; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -419,3 +423,35 @@ int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_req
 }
 
 }  // extern "C"
+
+int qkvf_layer_front(const void *x, int x_dtype, int64_t rows, const void *weight, float eps,
+                     float *stream, float *aux, void *out, hipStream_t hip_stream)
+{
+    if ((x_dtype != QKVF_DTYPE_BF16 && x_dtype != QKVF_DTYPE_F32) || !(eps >= 0.f) ||
+        !std::isfinite(eps))
+        return QKVF_ERR_SHAPE;
+    if (rows < 0 || rows > kLayerFrontMaxRows)
+        return QKVF_ERR_ROWS;
+    if (rows == 0)
+        return QKVF_OK;
+    if (!x || !stream || !out)
+        return QKVF_ERR_NULLPTR;
+    const bool f32 = x_dtype == QKVF_DTYPE_F32;
+    if (!aligned(x, f32 ? 32 : 16) || !aligned(stream, 32) || (aux && !aligned(aux, 32)) ||
+        !aligned(out, 16) || (weight && !aligned(weight, 16)))
+        return QKVF_ERR_ALIGN;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKVF_ERR_DEVICE;
+    if (t_lf_dev != dev) {
+        std::lock_guard<std::mutex> lock(g_mu);
+        int checked = 0;
+        const int ds = current_device(&checked);
+        if (ds != QKVF_OK)
+            return ds;
+        t_lf_dev = dev;
+    }
+    const hipError_t e =
+        launch_layer_front(x, f32, rows, weight, eps, stream, aux, out, hip_stream);
+    return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
+}

@@ -119,4 +119,10 @@ hipError_t launch_attn2(const void *q, int64_t q_stride, const void *gate, int64
                         int window, int Z, float *ws, void *out, int64_t out_stride,
                         hipStream_t stream);
 
+// LayerFront: rows of kHidden values, one block per row.
+constexpr int64_t kLayerFrontMaxRows = int64_t(1) << 20;
+hipError_t launch_layer_front(const void *x, bool x_fp32, int64_t rows, const void *weight,
+                              float eps, float *stream, float *aux, void *out,
+                              hipStream_t hip_stream);
+
 }  // namespace qkvf

@@ -74,7 +74,8 @@ def _load():
     lib.qkvfo_front.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_double, P, P, P, P, ctypes.c_int]
     lib.qkvfo_layer_front.restype = None
-    lib.qkvfo_layer_front.argtypes = [P, ctypes.c_int, ctypes.c_int64, P, ctypes.c_double, P, P, P]
+    lib.qkvfo_layer_front.argtypes = [P, ctypes.c_int, ctypes.c_int64, P, ctypes.c_double, P, P, P,
+                                      P]
     lib.qkvfo_attn2.restype = None
     lib.qkvfo_attn2.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int,
                                 P, ctypes.c_int64, P, ctypes.c_int, ctypes.c_int,
@@ -222,10 +223,12 @@ def attn2(q, gate, kv_cache, nkv: int, block_table, seq_lens, window: int = 0,
 LAYER_FRONT_EPS = 1e-6   # reading: the pre-QKV-projection norm's epsilon
 
 
-def layer_front(x, weight=None, eps: float = LAYER_FRONT_EPS, aux: bool = False):
+def layer_front(x, weight=None, eps: float = LAYER_FRONT_EPS, aux: bool = False,
+                exact: bool = False):
     """LayerFront of rows of 8192: x is uint16 bf16 bits or float32, shape
     [rows, 8192]; weight uint16 bf16 bits [8192] or None (a weightless norm).
-    Returns (stream fp32, aux fp32 or None, out uint16 bf16 bits)."""
+    Returns (stream fp32, aux fp32 or None, out uint16 bf16 bits), plus the
+    float64 values before rounding when exact=True."""
     lib = _load()
     x = np.asarray(x)
     if x.dtype == np.float32:
@@ -242,6 +245,7 @@ def layer_front(x, weight=None, eps: float = LAYER_FRONT_EPS, aux: bool = False)
     stream = np.empty((rows, HIDDEN), np.float32)
     a = np.empty((rows, HIDDEN), np.float32) if aux else None
     out = np.empty((rows, HIDDEN), np.uint16)
+    ex = np.empty((rows, HIDDEN), np.float64) if exact else None
     lib.qkvfo_layer_front(_ptr(x), is_fp32, rows, _ptr(w), float(eps), _ptr(stream), _ptr(a),
-                          _ptr(out))
-    return stream, a, out
+                          _ptr(out), _ptr(ex))
+    return (stream, a, out, ex) if exact else (stream, a, out)

@@ -25,7 +25,7 @@ import itertools
 import numpy as np
 
 from . import (HEAD_DIM, PAGE_SLOTS, QHEADS_PER_KV, attn2, bf16_to_float, epilogue,
-               head, n_cols, project, round_projection)
+               head, layer_front, n_cols, project, round_projection)
 
 RTOL = 1.6e-2
 ATOL = 2e-3
@@ -197,3 +197,44 @@ def check_attn2(out, q, gate, kv_cache, nkv: int, block_table, seq_lens, window:
     err = np.abs(got - want)
     return {"outputs": int(got.size), "max_abs_err": float(err.max()),
             "max_err_over_tol": float((err / (RTOL * np.abs(want) + ATOL)).max())}
+
+
+# LayerFront: a bf16 output whose exact value lies within this relative
+# distance of a rounding midpoint may round either way under fp32 arithmetic
+# (the row's fp32 sum of squares, the root and two products: < 2^-20).
+LF_TIE_REL = 2.0 ** -19
+
+
+def check_layer_front(x, weight, eps, stream, out, aux=None):
+    """Compare a LayerFront result with the oracle: stream and aux bit for
+    bit; out bit for bit except where the exact value is within LF_TIE_REL of
+    a bf16 rounding midpoint, where the other neighbour is also correct.
+    x: uint16 bf16 bits or float32 [rows, 8192]; outputs as numpy arrays
+    (stream / aux float32, out uint16)."""
+    want_s, want_a, want_o, ex = layer_front(x, weight, eps, aux=aux is not None, exact=True)
+    if not np.array_equal(np.asarray(stream).view(np.uint32), want_s.view(np.uint32)):
+        bad = np.argwhere(np.asarray(stream).view(np.uint32) != want_s.view(np.uint32))
+        raise ParityError(f"layer_front stream differs at {len(bad)} places, first {bad[0].tolist()}")
+    if aux is not None and not np.array_equal(np.asarray(aux).view(np.uint32),
+                                              want_a.view(np.uint32)):
+        raise ParityError("layer_front aux differs from the stream")
+    out = np.asarray(out, dtype=np.uint16)
+    diff = out != want_o
+    ties = 0
+    if diff.any():
+        g = bf16_to_float(out[diff]).astype(np.float64)
+        e = ex[diff]
+        # half a bf16 unit at e, plus the tie window
+        ae = np.abs(e)
+        expo = np.floor(np.log2(np.where(ae > 0, ae, 1.0)))
+        half = np.ldexp(1.0, (expo - 8).astype(np.int64))
+        ok = (ae > 0) & (np.abs(g - e) <= half + LF_TIE_REL * ae)
+        if not ok.all():
+            idx = np.argwhere(diff)[~ok][0]
+            r, k = int(idx[0]), int(idx[1])
+            raise ParityError(
+                f"layer_front out: {int((~ok).sum())} of {out.size} values wrong; first at row {r} "
+                f"column {k}: gpu {bf16_to_float(out[r, k])!r} oracle "
+                f"{bf16_to_float(want_o[r, k])!r} exact {ex[r, k]!r}")
+        ties = int(diff.sum())
+    return {"values": int(out.size), "tie_flips": ties}

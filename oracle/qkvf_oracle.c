@@ -301,10 +301,11 @@ void qkvfo_attn2(const uint16_t *q, int64_t q_stride, const uint16_t *gate,
  * usual RMS norm over the row with eps inside the root; w is the norm's
  * bf16 weight, or 1 when the norm has none (weight == NULL); the product is
  * rounded once, double -> binary32 -> bf16 as for every other output.
- * x_is_fp32 selects the input type (bf16 bits or fp32 values).
+ * x_is_fp32 selects the input type (bf16 bits or fp32 values).  `exact`, when
+ * not NULL, receives the double value before rounding (for the checker).
  */
 void qkvfo_layer_front(const void *x, int x_is_fp32, int64_t rows, const uint16_t *weight,
-                       double eps, float *stream, float *aux, uint16_t *out)
+                       double eps, float *stream, float *aux, uint16_t *out, double *exact)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
@@ -321,7 +322,10 @@ void qkvfo_layer_front(const void *x, int x_is_fp32, int64_t rows, const uint16_
             if (aux)
                 aux[r * HIDDEN + k] = s[k];
             const double w = weight ? qkvfo_bf16_to_double(weight[k]) : 1.0;
-            out[r * HIDDEN + k] = qkvfo_double_to_bf16((double)s[k] * rr * w);
+            const double v = (double)s[k] * rr * w;
+            if (exact)
+                exact[r * HIDDEN + k] = v;
+            out[r * HIDDEN + k] = qkvfo_double_to_bf16(v);
         }
     }
 }

@@ -108,3 +108,31 @@ def test_golden_three_four_by_hand():
         _, _, out = oracle.layer_front(xin)
         assert oracle.bf16_to_float(out[0, :2]).tolist() == g["expected_out_0_1"]
         assert np.all(out[0, 2:] == 0)
+
+
+def test_checker_accepts_the_oracle_and_rejects_flips():
+    from oracle import checker
+    rng = np.random.default_rng(6)
+    x = bits(rng.standard_normal((2, H)))
+    s, a, out = oracle.layer_front(x, aux=True)
+    checker.check_layer_front(x, None, EPS, s, out, aux=a)
+    bad = out.copy()
+    bad[1, 100] ^= 1                       # one unit away, far from a midpoint
+    _, _, _, ex = oracle.layer_front(x, exact=True)
+    v = ex[1, 100]
+    half = 2.0 ** (math.floor(math.log2(abs(v))) - 8)
+    if abs(abs(v) - (abs(oracle.bf16_to_float(out[1, 100])) + half)) > 1e-3 * half:
+        try:
+            checker.check_layer_front(x, None, EPS, s, bad, aux=a)
+        except checker.ParityError:
+            pass
+        else:
+            raise AssertionError("a one-unit flip passed")
+    s2 = s.copy()
+    s2[0, 5] = np.nextafter(s2[0, 5], np.float32(np.inf))
+    try:
+        checker.check_layer_front(x, None, EPS, s2, out, aux=a)
+    except checker.ParityError:
+        pass
+    else:
+        raise AssertionError("a stream difference passed")
