@@ -71,6 +71,9 @@ def parse():
                     help="also time every workload and sweep point; one JSON line each on stderr")
     ap.add_argument("--attn2", default="", metavar="WORKLOAD",
                     help="time attn2 instead of the front: one of " + ", ".join(wl.ATTN2_WORKLOADS))
+    ap.add_argument("--layer-front", default="", metavar="WORKLOAD",
+                    help="time LayerFront instead of the front: one of "
+                         + ", ".join(wl.LAYER_FRONT_WORKLOADS))
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="instead of the front, time device-to-device copies of MB megabytes "
                          "(a plain copy kernel of known size, for scaling memory counters)")
@@ -272,6 +275,86 @@ def attn2_line(a: wl.Attn2Workload, args) -> dict:
     }
 
 
+def time_layer_front(w: wl.LayerFrontWorkload, steps: int, warmup: int, repeats: int):
+    """Calls rotate over input/output sets of >= 600 MB in total, so every
+    call's rows come from HBM."""
+    dev = "cuda"
+    per_set = w.algorithmic_bytes()
+    sets = max(2, int(600e6 // per_set) + 1)
+    xs = [wl.make_lf_x(w, s, device=dev) for s in range(min(sets, 64))]
+    # beyond 64 distinct inputs, further sets reuse their x (only the
+    # buffers differ, which keeps generation fast)
+    xs = [xs[s % len(xs)].clone() if s >= len(xs) else xs[s] for s in range(sets)]
+    weight = wl.make_lf_weight(w, device=dev)
+    st = [torch.empty(w.rows, wl.HIDDEN, device=dev) for _ in range(sets)]
+    ax = [torch.empty(w.rows, wl.HIDDEN, device=dev) for _ in range(sets)] if w.aux else None
+    out = [torch.empty(w.rows, wl.HIDDEN, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    stream = torch.cuda.Stream()
+
+    def call(i):
+        s = i % sets
+        qf.layer_front(xs[s], st[s], out[s], aux=None if ax is None else ax[s], weight=weight,
+                       stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            call(warmup + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / steps)
+    return sorted(times)[len(times) // 2], times, sets
+
+
+def layer_front_cpu_baseline(w: wl.LayerFrontWorkload, budget_s: float) -> dict | None:
+    if budget_s <= 0:
+        return None
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    x = wl.make_lf_x(w, 0)
+    xn = x.numpy() if w.fp32_input else wl.bits(x)
+    weight = wl.make_lf_weight(w)
+    wn = None if weight is None else wl.bits(weight)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.layer_front(xn, wn, aux=w.aux)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (el / calls) * (calls + 1) > 2 * budget_s:
+            break
+    per_call = el / calls
+    return {"value": round(w.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
+            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "kind": "oracle",
+            "sample": f"{calls} full oracle calls of {w.name} (input set 0), OpenMP over rows"}
+
+
+def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
+    ms, times, sets = time_layer_front(w, args.steps, args.warmup, args.repeats)
+    nbytes = w.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "LayerFront achieved HBM GB/s (algorithmic bytes per call / time per call)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.fp32_input else "bf16", "data": "synthetic",
+        "config": dict(wl.describe_layer_front(w), sets_rotated=sets,
+                       algorithmic_bytes_per_call=nbytes),
+        "roofline": {"bound": "hbm", "kernel": "layer_front (the whole call)",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "repeats_ms": [round(t, 6) for t in times],
+    }
+
+
 def rotated_sets(w: wl.Workload, requested: int) -> int:
     sets = requested or w.wsets
     # enough weight sets that the rotation exceeds the 256 MB MALL
@@ -310,6 +393,14 @@ def main():
     if a.copy_calibration > 0:
         copy_calibration(a.copy_calibration, a.steps)
         return
+    if a.layer_front:
+        if a.layer_front not in wl.LAYER_FRONT_WORKLOADS:
+            raise SystemExit(f"unknown LayerFront workload {a.layer_front}")
+        lw = wl.LAYER_FRONT_WORKLOADS[a.layer_front]
+        line = layer_front_line(lw, a)
+        line["cpu_baseline"] = layer_front_cpu_baseline(lw, a.cpu_baseline_seconds)
+        print(json.dumps(line), flush=True)
+        return
     if a.attn2:
         if a.attn2 not in wl.ATTN2_WORKLOADS:
             raise SystemExit(f"unknown attn2 workload {a.attn2}")
@@ -342,6 +433,12 @@ def main():
                               "us_per_call": line["us_per_call"], "GB_per_s": line["value"],
                               "frac_of_8TBs": line["roofline"]["frac"],
                               "request_sets_rotated": line["config"]["request_sets_rotated"]}),
+                  file=sys.stderr, flush=True)
+        for lw in wl.LAYER_FRONT_WORKLOADS.values():
+            line = layer_front_line(lw, a)
+            print(json.dumps({"workload": lw.name, "us_per_call": line["us_per_call"],
+                              "GB_per_s": line["value"], "frac_of_8TBs": line["roofline"]["frac"],
+                              "sets_rotated": line["config"]["sets_rotated"]}),
                   file=sys.stderr, flush=True)
     base = cpu_baseline(w, a.cpu_baseline_seconds)
     traffic = measured_traffic(w)

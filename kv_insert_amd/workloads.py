@@ -26,6 +26,11 @@ head_dim 64, 8 q heads per KV head, an optional window):
             set of distinct pages (disjoint across requests and sets), the
             unused tail of each row points at page 0;
   seq_lens  int32 [R], per workload.
+
+LayerFront (layer_front page, LayerFront.run; rows of 8192):
+  x         bf16 or fp32 [rows, 8192] ~ N(0, 1) (the embedded tokens; the
+            bf16 path is the eager embedding, the fp32 one the in-graph one);
+  weight    bf16 [8192] = 1 + 0.1 N(0, 1) (the pre-QKV norm's gain), or none.
 """
 from __future__ import annotations
 
@@ -315,3 +320,46 @@ def describe_attn2(a: Attn2Workload) -> dict:
     return {"workload": a.name, "requests": a.R, "query_rows": 8 * a.R, "num_kv_heads": a.nkv,
             "seq_lens": list(a.lens), "max_model_len": a.max_model_len, "window": a.window,
             "cache_pages": a.pages}
+
+
+# ---------------------------------------------------------- LayerFront --
+
+@dataclasses.dataclass(frozen=True)
+class LayerFrontWorkload:
+    name: str
+    rows: int
+    fp32_input: bool
+    weight: bool = True
+    aux: bool = True
+    index: int = 0
+
+    def algorithmic_bytes(self) -> int:
+        """x read, stream (+ aux) written as fp32, out written as bf16, the
+        weight read once."""
+        n = self.rows * HIDDEN
+        return (n * (4 if self.fp32_input else 2) + n * 4 * (2 if self.aux else 1) + n * 2
+                + (2 * HIDDEN if self.weight else 0))
+
+
+LF1 = LayerFrontWorkload("lf_m16_bf16_w_aux", rows=16, fp32_input=False, index=21)
+LF2 = LayerFrontWorkload("lf_m8_f32_w", rows=8, fp32_input=True, aux=False, index=22)
+LF3 = LayerFrontWorkload("lf_m1_bf16_w", rows=1, fp32_input=False, aux=False, index=23)
+LAYER_FRONT_WORKLOADS = {w.name: w for w in (LF1, LF2, LF3)}
+
+
+def make_lf_x(w: LayerFrontWorkload, set_index: int = 0, device="cpu") -> torch.Tensor:
+    g = _gen((1000 * w.index + set_index) * 7919 + 9)
+    x = torch.randn(w.rows, HIDDEN, generator=g)
+    return (x if w.fp32_input else x.to(torch.bfloat16)).to(device)
+
+
+def make_lf_weight(w: LayerFrontWorkload, device="cpu"):
+    if not w.weight:
+        return None
+    g = _gen(1000 * w.index * 7919 + 10)
+    return (1.0 + 0.1 * torch.randn(HIDDEN, generator=g)).to(torch.bfloat16).to(device)
+
+
+def describe_layer_front(w: LayerFrontWorkload) -> dict:
+    return {"workload": w.name, "rows": w.rows, "hidden": HIDDEN,
+            "x_dtype": "fp32" if w.fp32_input else "bf16", "weight": w.weight, "aux": w.aux}
