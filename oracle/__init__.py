@@ -76,6 +76,10 @@ def _load():
     lib.qkvfo_layer_front.restype = None
     lib.qkvfo_layer_front.argtypes = [P, ctypes.c_int, ctypes.c_int64, P, ctypes.c_double, P, P, P,
                                       P]
+    lib.qkvfo_route_score.restype = ctypes.c_float
+    lib.qkvfo_route_score.argtypes = [ctypes.c_float]
+    lib.qkvfo_route.restype = None
+    lib.qkvfo_route.argtypes = [P, ctypes.c_int64, P, ctypes.c_double, ctypes.c_int, P, P]
     lib.qkvfo_attn2.restype = None
     lib.qkvfo_attn2.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int,
                                 P, ctypes.c_int64, P, ctypes.c_int, ctypes.c_int,
@@ -249,3 +253,27 @@ def layer_front(x, weight=None, eps: float = LAYER_FRONT_EPS, aux: bool = False,
     lib.qkvfo_layer_front(_ptr(x), is_fp32, rows, _ptr(w), float(eps), _ptr(stream), _ptr(a),
                           _ptr(out), _ptr(ex))
     return (stream, a, out, ex) if exact else (stream, a, out)
+
+
+ROUTE_EXPERTS = 256
+ROUTE_TOP_K = 8
+ROUTE_DIVISION_EPS = 1e-15   # the page's division epsilon
+
+
+def route_score(logit: float) -> float:
+    """The fp32 sigmoid score of one logit (the exact sigmoid rounded once)."""
+    return float(_load().qkvfo_route_score(float(logit)))
+
+
+def route(logits, bias, route_scale: float):
+    """MuseRouting of fp32 logits [b, >= 256] with an fp32 bias [256]:
+    returns (ids int32 [b, 8], weights fp32 [b, 8]), best first."""
+    lib = _load()
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    b = np.ascontiguousarray(bias, dtype=np.float32)
+    assert lg.ndim == 2 and lg.shape[1] >= ROUTE_EXPERTS and b.shape == (ROUTE_EXPERTS,)
+    tokens = lg.shape[0]
+    ids = np.empty((tokens, ROUTE_TOP_K), np.int32)
+    w = np.empty((tokens, ROUTE_TOP_K), np.float32)
+    lib.qkvfo_route(_ptr(lg), lg.shape[1], _ptr(b), float(route_scale), tokens, _ptr(ids), _ptr(w))
+    return ids, w

@@ -329,3 +329,54 @@ void qkvfo_layer_front(const void *x, int x_is_fp32, int64_t rows, const uint16_
         }
     }
 }
+
+/*
+ * MuseRouting (cute_ops page, MuseRouting entry and class; unsupported_router
+ * for the constants): routing of b <= 8 tokens over 256 experts.
+ *     score[e] = sigmoid(logit[e])              (fp32)
+ *     key[e]   = score[e] + bias[e]             (fp32; the correction bias
+ *                                                steers the selection only)
+ *     the 8 experts with the largest keys, best first
+ *     weight   = score * route_scale / (sum of the 8 scores + 1e-15)
+ * Readings (the page names the steps but not their arithmetic): the score
+ * is the sigmoid's exact value rounded once to fp32 (computed in double);
+ * the key is the fp32 sum; equal keys rank by lower expert id; ids and
+ * weights are written best first; the weight is computed in double from the
+ * fp32 scores, the 8 scores summed best first, and rounded once to fp32.
+ */
+#define ROUTE_EXPERTS 256
+#define ROUTE_TOP_K 8
+
+float qkvfo_route_score(float logit) { return (float)(1.0 / (1.0 + exp(-(double)logit))); }
+
+void qkvfo_route(const float *logits, int64_t row_stride, const float *bias, double route_scale,
+                 int tokens, int32_t *ids, float *weights)
+{
+    for (int t = 0; t < tokens; ++t) {
+        const float *row = logits + (int64_t)t * row_stride;
+        float score[ROUTE_EXPERTS], key[ROUTE_EXPERTS];
+        int taken[ROUTE_EXPERTS];
+        for (int e = 0; e < ROUTE_EXPERTS; ++e) {
+            score[e] = qkvfo_route_score(row[e]);
+            key[e] = score[e] + bias[e];
+            taken[e] = 0;
+        }
+        int pick[ROUTE_TOP_K];
+        for (int k = 0; k < ROUTE_TOP_K; ++k) {
+            int best = -1;
+            for (int e = 0; e < ROUTE_EXPERTS; ++e)
+                if (!taken[e] && (best < 0 || key[e] > key[best]))
+                    best = e;      /* strict '>' keeps the lower id on equal keys */
+            taken[best] = 1;
+            pick[k] = best;
+        }
+        double sum = 0.0;
+        for (int k = 0; k < ROUTE_TOP_K; ++k)
+            sum += (double)score[pick[k]];
+        for (int k = 0; k < ROUTE_TOP_K; ++k) {
+            ids[t * ROUTE_TOP_K + k] = pick[k];
+            weights[t * ROUTE_TOP_K + k] =
+                (float)((double)score[pick[k]] * route_scale / (sum + 1e-15));
+        }
+    }
+}
