@@ -246,6 +246,35 @@ int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_req
 int qkvf_layer_front(const void *x, int x_dtype, int64_t rows, const void *weight, float eps,
                      float *stream, float *aux, void *out, hipStream_t hip_stream);
 
+/*
+ * MuseRouting: the routing of one MoE layer for decode batches of 1 to 8
+ * tokens (cute_ops page, MuseRouting entry and class; unsupported_router for
+ * the constants: sigmoid scores, top-8 of 256 experts, division epsilon
+ * 1e-15).  For each token t:
+ *     score[e] = sigmoid(logits[t][e])        fp32, the exact sigmoid rounded once
+ *     key[e]   = score[e] + bias[e]           fp32 (the correction bias steers the
+ *                                             selection only)
+ *     ids[t]   = the 8 experts with the largest keys, best first; equal keys
+ *                rank by lower expert id
+ *     weights[t][k] = score[ids[t][k]] * route_scale / (sum of the 8 scores + 1e-15)
+ *                computed in double (the scores summed best first), rounded once
+ *                to fp32.
+ * The router's output multiplier must already be folded into its weight, so
+ * the logits are final.  Device pointers: logits fp32 [num_tokens] rows of
+ * >= 256 values, row stride logits_row_stride elements (a multiple of 4, so
+ * every row is 16-byte aligned), 16-byte aligned; bias fp32 [256], 16-byte
+ * aligned; ids int32 [num_tokens][8] and weights fp32 [num_tokens][8],
+ * 4-byte aligned, written.  Logits and bias must be finite.  One launch on
+ * `stream`; allocates nothing, never synchronizes (graph-capturable).  The
+ * routing metadata for other systems' MoE GEMMs is not produced.
+ * Errors: QKVF_ERR_ROWS (num_tokens outside [1, 8]), QKVF_ERR_SHAPE (row
+ * stride below 256, route_scale not finite), QKVF_ERR_NULLPTR,
+ * QKVF_ERR_ALIGN, QKVF_ERR_DEVICE, QKVF_ERR_HIP.
+ */
+int qkvf_route(const float *logits, int64_t logits_row_stride, const float *bias,
+               double route_scale, int num_tokens, int32_t *ids, float *weights,
+               hipStream_t stream);
+
 /* Free the workspace of every device and forget prepared shapes.  No call
  * may be in flight. */
 void qkvf_release(void);

@@ -28,7 +28,7 @@ STATUS = {
 }
 EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
            "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_device_fault", "qkvf_release",
-           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front")
+           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front", "qkvf_route")
 
 
 class QkvfError(ValueError):
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.qkvf_attn2_plan.restype = I
     L.qkvf_layer_front.argtypes = [P, I, I64, P, ctypes.c_float, P, P, P, P]
     L.qkvf_layer_front.restype = I
+    L.qkvf_route.argtypes = [P, I64, P, ctypes.c_double, I, P, P, P]
+    L.qkvf_route.restype = I
     L.qkvf_release.argtypes = []
     L.qkvf_release.restype = None
     _lib = L
@@ -206,3 +208,11 @@ def layer_front(x, stream_out, out, aux=None, weight=None, eps: float = 1e-6, st
     st = lib().qkvf_layer_front(_ptr(x), dt, int(x.shape[0]), _ptr(weight), float(eps),
                                 _ptr(stream_out), _ptr(aux), _ptr(out), _stream_handle(stream))
     _raise(st, "qkvf_layer_front")
+
+
+def route(logits, bias, route_scale: float, ids, weights, stream=None) -> None:
+    """qkvf_route on torch tensors: logits fp32 [b, >= 256] (rows 16-byte
+    aligned), bias fp32 [256], ids int32 [b, 8], weights fp32 [b, 8]."""
+    st = lib().qkvf_route(_ptr(logits), logits.stride(0), _ptr(bias), float(route_scale),
+                          int(logits.shape[0]), _ptr(ids), _ptr(weights), _stream_handle(stream))
+    _raise(st, "qkvf_route")

@@ -44,7 +44,8 @@ struct Attn2Config {
 };
 thread_local Attn2Config t_attn2;
 
-// The device this thread last checked for qkvf_layer_front (-1: none).
+// The device this thread last checked for qkvf_layer_front and qkvf_route
+// (-1: none).
 thread_local int t_lf_dev = -1;
 
 bool valid_nkv(int nkv) { return nkv == 1 || nkv == 2 || nkv == 4 || nkv == 8; }
@@ -424,6 +425,25 @@ int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_req
 
 }  // extern "C"
 
+namespace {
+// The current device, checked to be a gfx950 once per thread and device.
+int checked_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKVF_ERR_DEVICE;
+    if (t_lf_dev != dev) {
+        std::lock_guard<std::mutex> lock(g_mu);
+        int checked = 0;
+        const int ds = current_device(&checked);
+        if (ds != QKVF_OK)
+            return ds;
+        t_lf_dev = dev;
+    }
+    return QKVF_OK;
+}
+}  // namespace
+
 int qkvf_layer_front(const void *x, int x_dtype, int64_t rows, const void *weight, float eps,
                      float *stream, float *aux, void *out, hipStream_t hip_stream)
 {
@@ -440,18 +460,31 @@ int qkvf_layer_front(const void *x, int x_dtype, int64_t rows, const void *weigh
     if (!aligned(x, f32 ? 32 : 16) || !aligned(stream, 32) || (aux && !aligned(aux, 32)) ||
         !aligned(out, 16) || (weight && !aligned(weight, 16)))
         return QKVF_ERR_ALIGN;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return QKVF_ERR_DEVICE;
-    if (t_lf_dev != dev) {
-        std::lock_guard<std::mutex> lock(g_mu);
-        int checked = 0;
-        const int ds = current_device(&checked);
-        if (ds != QKVF_OK)
-            return ds;
-        t_lf_dev = dev;
-    }
+    const int ds = checked_device();
+    if (ds != QKVF_OK)
+        return ds;
     const hipError_t e =
         launch_layer_front(x, f32, rows, weight, eps, stream, aux, out, hip_stream);
+    return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
+}
+
+int qkvf_route(const float *logits, int64_t logits_row_stride, const float *bias,
+               double route_scale, int num_tokens, int32_t *ids, float *weights,
+               hipStream_t stream)
+{
+    if (num_tokens < 1 || num_tokens > kRouteMaxTokens)
+        return QKVF_ERR_ROWS;
+    if (logits_row_stride < kRouteExperts || !std::isfinite(route_scale))
+        return QKVF_ERR_SHAPE;
+    if (!logits || !bias || !ids || !weights)
+        return QKVF_ERR_NULLPTR;
+    if (!aligned(logits, 16) || logits_row_stride % 4 || !aligned(bias, 16) || !aligned(ids, 4) ||
+        !aligned(weights, 4))
+        return QKVF_ERR_ALIGN;
+    const int ds = checked_device();
+    if (ds != QKVF_OK)
+        return ds;
+    const hipError_t e = launch_route(logits, logits_row_stride, bias, route_scale, num_tokens,
+                                      ids, weights, stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }

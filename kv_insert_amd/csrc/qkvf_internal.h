@@ -125,4 +125,13 @@ hipError_t launch_layer_front(const void *x, bool x_fp32, int64_t rows, const vo
                               float eps, float *stream, float *aux, void *out,
                               hipStream_t hip_stream);
 
+// MuseRouting: top-8 of 256 experts for up to 8 tokens, one wave per token.
+constexpr int kRouteExperts = 256;
+constexpr int kRouteTopK = 8;
+constexpr int kRouteMaxTokens = 8;
+constexpr double kRouteDivisionEps = 1e-15;
+hipError_t launch_route(const float *logits, int64_t row_stride, const float *bias,
+                        double route_scale, int tokens, int32_t *ids, float *weights,
+                        hipStream_t stream);
+
 }  // namespace qkvf

@@ -173,3 +173,26 @@ def test_attn2_run_without_prepare_is_refused(L):
     t.start()
     t.join()
     assert res == [6]
+
+
+def test_route_refusals_before_the_device(L):
+    P = 1 << 20
+    assert L.qkvf_route(P, 256, P, 1.0, 0, P, P, None) == 3
+    assert L.qkvf_route(P, 256, P, 1.0, 9, P, P, None) == 3
+    assert L.qkvf_route(P, 255, P, 1.0, 1, P, P, None) == 2
+    assert L.qkvf_route(P, 256, P, float("nan"), 1, P, P, None) == 2
+    assert L.qkvf_route(None, 256, P, 1.0, 1, P, P, None) == 5
+    assert L.qkvf_route(P + 4, 256, P, 1.0, 1, P, P, None) == 4
+    assert L.qkvf_route(P, 258, P, 1.0, 1, P, P, None) == 4
+
+
+def test_layer_front_refusals_before_the_device(L):
+    P = 1 << 20
+    assert L.qkvf_layer_front(P, 2, 1, None, 1e-6, P, None, P, None) == 2
+    assert L.qkvf_layer_front(P, 0, 1, None, -1.0, P, None, P, None) == 2
+    assert L.qkvf_layer_front(P, 0, -1, None, 1e-6, P, None, P, None) == 3
+    assert L.qkvf_layer_front(P, 0, (1 << 20) + 1, None, 1e-6, P, None, P, None) == 3
+    assert L.qkvf_layer_front(P, 0, 0, None, 1e-6, P, None, P, None) == 0
+    assert L.qkvf_layer_front(None, 0, 1, None, 1e-6, P, None, P, None) == 5
+    assert L.qkvf_layer_front(P + 16, 1, 1, None, 1e-6, P, None, P, None) == 4
+    assert L.qkvf_layer_front(P, 0, 1, P + 2, 1e-6, P, None, P, None) == 4
