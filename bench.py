@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--layer-front", default="", metavar="WORKLOAD",
                     help="time LayerFront instead of the front: one of "
                          + ", ".join(wl.LAYER_FRONT_WORKLOADS))
+    ap.add_argument("--route", default="", metavar="WORKLOAD",
+                    help="time MuseRouting instead of the front: one of "
+                         + ", ".join(wl.ROUTE_WORKLOADS))
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="instead of the front, time device-to-device copies of MB megabytes "
                          "(a plain copy kernel of known size, for scaling memory counters)")
@@ -355,6 +358,66 @@ def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
     }
 
 
+def route_line(w: wl.RouteWorkload, args) -> dict:
+    """MuseRouting calls rotate over 64 input sets (the data are a few KB)."""
+    dev = "cuda"
+    sets = 64
+    inputs = [wl.make_route_inputs(w, s, device=dev) for s in range(sets)]
+    ids = [torch.empty(w.tokens, 8, dtype=torch.int32, device=dev) for _ in range(sets)]
+    wts = [torch.empty(w.tokens, 8, device=dev) for _ in range(sets)]
+    stream = torch.cuda.Stream()
+
+    def call(i):
+        s = i % sets
+        qf.route(inputs[s][0], inputs[s][1], w.route_scale, ids[s], wts[s], stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            call(i)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            call(args.warmup + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / args.steps)
+    ms = sorted(times)[len(times) // 2]
+    nbytes = w.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    base = None
+    if args.cpu_baseline_seconds > 0:
+        import oracle
+        lg, bs = wl.make_route_inputs(w, 0)
+        lg, bs = lg.numpy(), bs.numpy()
+        calls, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_baseline_seconds, 2.0):
+            oracle.route(lg, bs, w.route_scale)
+            calls += 1
+        per = (time.perf_counter() - t0) / calls
+        base = {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s",
+                "us_per_call": round(per * 1e6, 2), "cores": 1, "kind": "oracle",
+                "sample": f"{calls} full oracle calls of {w.name} (input set 0), one thread"}
+    return {
+        "metric": "MuseRouting us per call (and algorithmic GB/s)",
+        "value": round(gbs, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "experts": 256, "top_k": 8,
+                   "route_scale": w.route_scale, "algorithmic_bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "route (the whole call)", "achieved": round(gbs, 3),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6),
+                     "traffic": None},
+        "cpu_baseline": base,
+        "repeats_ms": [round(t, 6) for t in times],
+    }
+
+
 def rotated_sets(w: wl.Workload, requested: int) -> int:
     sets = requested or w.wsets
     # enough weight sets that the rotation exceeds the 256 MB MALL
@@ -392,6 +455,11 @@ def main():
     torch.cuda.set_device(0)
     if a.copy_calibration > 0:
         copy_calibration(a.copy_calibration, a.steps)
+        return
+    if a.route:
+        if a.route not in wl.ROUTE_WORKLOADS:
+            raise SystemExit(f"unknown routing workload {a.route}")
+        print(json.dumps(route_line(wl.ROUTE_WORKLOADS[a.route], a)), flush=True)
         return
     if a.layer_front:
         if a.layer_front not in wl.LAYER_FRONT_WORKLOADS:

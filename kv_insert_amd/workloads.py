@@ -27,6 +27,10 @@ head_dim 64, 8 q heads per KV head, an optional window):
             unused tail of each row points at page 0;
   seq_lens  int32 [R], per workload.
 
+MuseRouting (cute_ops page, MuseRouting entry; 256 experts, top 8):
+  logits    fp32 [b, 256] ~ N(0, 2^2) (router logits of b <= 8 tokens);
+  bias      fp32 [256] ~ N(0, 0.05^2) (the correction bias); route_scale 2.5.
+
 LayerFront (layer_front page, LayerFront.run; rows of 8192):
   x         bf16 or fp32 [rows, 8192] ~ N(0, 1) (the embedded tokens; the
             bf16 path is the eager embedding, the fp32 one the in-graph one);
@@ -363,3 +367,29 @@ def make_lf_weight(w: LayerFrontWorkload, device="cpu"):
 def describe_layer_front(w: LayerFrontWorkload) -> dict:
     return {"workload": w.name, "rows": w.rows, "hidden": HIDDEN,
             "x_dtype": "fp32" if w.fp32_input else "bf16", "weight": w.weight, "aux": w.aux}
+
+
+# ------------------------------------------------------------- routing --
+
+@dataclasses.dataclass(frozen=True)
+class RouteWorkload:
+    name: str
+    tokens: int
+    route_scale: float = 2.5
+    index: int = 0
+
+    def algorithmic_bytes(self) -> int:
+        """logits and bias read, ids and weights written."""
+        return 4 * 256 * self.tokens + 4 * 256 + 2 * 4 * 8 * self.tokens
+
+
+RT1 = RouteWorkload("route_b8", tokens=8, index=31)
+RT2 = RouteWorkload("route_b1", tokens=1, index=32)
+ROUTE_WORKLOADS = {w.name: w for w in (RT1, RT2)}
+
+
+def make_route_inputs(w: RouteWorkload, set_index: int = 0, device="cpu"):
+    g = _gen((1000 * w.index + set_index) * 7919 + 11)
+    logits = torch.randn(w.tokens, 256, generator=g) * 2.0
+    bias = torch.randn(256, generator=g) * 0.05
+    return logits.to(device), bias.to(device)
