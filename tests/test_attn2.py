@@ -306,3 +306,47 @@ def test_front_then_attn2():
     cache_gpu = g["kv_cache"].cpu()
     out = run_attn2(case, "after-front", y=y_gpu, cache=cache_gpu)
     case.oracle_check(to_bits(out), y=y_gpu, cache=cache_gpu)
+
+
+def test_layer_front_then_front_then_attn2():
+    """The first layer's decode step, each stage fed the previous stage's
+    device output: LayerFront turns 8 embedded rows into x, the front
+    projects x and inserts the 8 verify tokens' K|V into the request's pages,
+    attn2 attends over the cache.  Every stage matches the oracle on the
+    bytes it was given."""
+    from helpers import Case, check
+    nkv, L = 2, 1000
+    a = wl.Attn2Workload("chain", nkv=nkv, max_model_len=4096, lens=(L,), index=36)
+    case = Attn2Case(a)
+    pages = case.cache.shape[0]
+    w = dataclasses.replace(wl.C2, pages=pages, slot_hi=pages * 16 - 7)
+    front = Case(w)
+    # LayerFront: fp32 embedded rows -> stream, out = the front's x
+    g = torch.Generator().manual_seed(36)
+    emb = torch.randn(8, wl.HIDDEN, generator=g)
+    norm_w = (1.0 + 0.1 * torch.randn(wl.HIDDEN, generator=g)).to(torch.bfloat16)
+    emb_d = emb.cuda()
+    stream = torch.empty(8, wl.HIDDEN, device="cuda")
+    x_d = torch.empty(8, wl.HIDDEN, dtype=torch.bfloat16, device="cuda")
+    say("chain: layer_front")
+    qf.layer_front(emb_d, stream, x_d, weight=norm_w.cuda(), eps=1e-6)
+    torch.cuda.synchronize()
+    checker.check_layer_front(emb.numpy(), to_bits(norm_w), 1e-6, stream.cpu().numpy(),
+                              to_bits(x_d.cpu()))
+    # the front on that x, inserting the verify tokens at positions L-8 .. L-1
+    front.x = x_d.cpu()
+    front.positions = torch.arange(L - 8, L, dtype=torch.int64)
+    front.slots = torch.tensor([int(case.table[0, p // 16]) * 16 + p % 16
+                                for p in range(L - 8, L)], dtype=torch.int64)
+    front.cache = case.cache.clone()
+    gd = front.device()
+    say("chain: front")
+    qf.prepare(front.N, nkv, 8)
+    qf.run(gd["x"], gd["W"], gd["positions"], gd["slots"], gd["cos_sin"], gd["y"], gd["kv_cache"], M=8)
+    torch.cuda.synchronize()
+    assert qf.device_fault() == 0
+    check(front, gd)
+    # attn2 on the front's y and cache
+    y_gpu, cache_gpu = gd["y"].cpu(), gd["kv_cache"].cpu()
+    out = run_attn2(case, "chain", y=y_gpu, cache=cache_gpu)
+    case.oracle_check(to_bits(out), y=y_gpu, cache=cache_gpu)
