@@ -51,7 +51,10 @@ constexpr int kGroups = QKVF_ATTN2_GROUPS;     // key groups (chunks) per step
 constexpr int kStep = kChunk * kGroups;        // keys per step
 constexpr int kThreads = 256 * kGroups;        // 4 query waves per key group
 constexpr int kDepth = QKVF_ATTN2_DEPTH;       // steps of loads in flight
-constexpr int kSegKeys = 2048 / kStep * kStep; // keys per segment: whole steps
+// Page offsets are staged per segment of keys; a split of up to 4096 keys
+// (a 128K context over 32 splits) is one segment, so its ring never drains
+// for a restage.
+constexpr int kSegKeys = 4096 / kStep * kStep; // keys per segment: whole steps
 constexpr int kSegPages = kSegKeys / kPageSlots;
 // Splits are whole steps of at least kAttn2MinSplitKeys keys.
 constexpr int kMinSplitChunks = (kAttn2MinSplitKeys / kChunk + kGroups - 1) / kGroups * kGroups;

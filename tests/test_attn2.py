@@ -142,6 +142,37 @@ def test_attn2_max_requests():
     case.oracle_check(to_bits(run_attn2(case, b.name)))
 
 
+def shared_page_case(a: wl.Attn2Workload, seed: int) -> Attn2Case:
+    """An Attn2Case whose requests all read one set of pages (enough for
+    max_model_len), each through its own random permutation of the block
+    table: attention only reads the cache, so long contexts over many
+    requests need no more than one request's pages."""
+    case = Attn2Case.__new__(Attn2Case)
+    case.a, case.nkv, case.window = a, a.nkv, a.eff_window
+    case.y = wl.make_attn2_y(a, 0)
+    pages = a.table_width
+    g = torch.Generator().manual_seed(seed)
+    case.cache = torch.randn(pages, a.nkv, wl.PAGE_SLOTS, wl.SLOT_WIDTH,
+                             generator=g).to(torch.bfloat16)
+    case.table = torch.stack([torch.randperm(pages, generator=g) for _ in a.lens]).to(torch.int32)
+    case.lens = wl.make_attn2_lens(a)
+    return case
+
+
+@pytest.mark.parametrize("window", [0, 6000])
+def test_attn2_multi_segment_splits(window):
+    """With one split per (request, KV head) a block walks the request's whole
+    context, so lengths past 4096 keys cross the segments in which the kernel
+    stages page offsets, at and around the segment edges; with a window the
+    walk starts in the middle of a page."""
+    lens = (4096, 4097, 4100, 8192, 5000, 8191, 6000, 7777) * 4
+    a = wl.Attn2Workload(f"multi_segment_w{window}", nkv=8, max_model_len=8192, lens=lens,
+                         window=window, index=41)
+    assert qf.attn2_plan(a.nkv, a.max_model_len, a.eff_window, a.R) == 1
+    case = shared_page_case(a, seed=41 + window)
+    case.oracle_check(to_bits(run_attn2(case, a.name)))
+
+
 def test_attn2_needles_at_split_and_page_edges():
     """Each (row, head) query is a scaled copy of one key, so its softmax is
     concentrated there: a key lost at a split, chunk or page edge shows."""
