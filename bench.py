@@ -35,6 +35,8 @@ COUNTERS = os.path.join(ROOT, "profiles", "front_fused_counters.json")
 
 ATTN2_SRC = os.path.join(ROOT, "kv_insert_amd", "csrc", "qkvf_attn2.hip")
 ATTN2_COUNTERS = os.path.join(ROOT, "profiles", "attn2_counters.json")
+LF_SRC = os.path.join(ROOT, "kv_insert_amd", "csrc", "qkvf_layer_front.hip")
+LF_COUNTERS = os.path.join(ROOT, "profiles", "layer_front_counters.json")
 
 
 def kernel_hash(path: str = KERNEL_SRC) -> str:
@@ -353,7 +355,8 @@ def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
                        algorithmic_bytes_per_call=nbytes),
         "roofline": {"bound": "hbm", "kernel": "layer_front (the whole call)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w, LF_COUNTERS, LF_SRC)},
         "repeats_ms": [round(t, 6) for t in times],
     }
 

@@ -10,25 +10,30 @@
 // max(0, L - 8 + t - W + 1).  The output row is, per query head h (KV head
 // h / 8), o / sqrt(mean(o^2) + eps) * sigmoid(gate), o = softmax(scale q K^T) V.
 //
-// attn2_split: one block of 4 waves per (key split z, KV head j, request r).
-// Its 64 query rows are the 8 tokens x 8 q heads of KV head j; wave w owns
-// q heads 2w, 2w + 1 (16 rows, row c = 8 (h - 2w) + t).  The split's page
-// numbers are staged in LDS first, so K|V loads never wait on a table read;
-// keys then stream in chunks of 32 (two pages of 16 slots) with kDepth
-// chunks of loads in flight per thread (a register ring), each chunk staged
-// in LDS as K [32 keys][64] (16-byte pieces XOR-swizzled by key) and
-// V^T [64][32 keys] (groups of 4 keys XOR-swizzled by dimension / 8):
+// attn2_split: one block of 16 waves per (key split z, KV head j, request
+// r), 4 key groups x 4 query waves.  The 64 query rows are the 8 tokens x 8
+// q heads of KV head j; query wave w owns q heads 2w, 2w + 1 (16 rows, row
+// c = 8 (h - 2w) + t) in every key group.  The split's page offsets are
+// staged in LDS per segment of keys, so K|V loads never wait on a table
+// read.  Keys then stream in steps of 128 (one chunk of 32 per key group):
+// each thread loads one 16-byte piece of K and of V of one slot, with
+// kDepth steps of loads in flight (a register ring), and stages them in LDS
+// as K [128 keys][64] (16-byte pieces XOR-swizzled by key) and, per key
+// group, V^T [64][32 keys] (groups of 4 keys XOR-swizzled by dimension).
+// Each key group's waves then take their 32 keys:
 //   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, A = 16 keys, B = 16 query rows;
 //                 lane l holds query l % 16 and keys 4 (l / 16) + v),
-//   online softmax per query (max over the lane's 8 keys, then across the 4
-//                 lane groups holding the same query),
+//   weights 2^(scale s - m) against a reference point m that trails the
+//                 running max by at most 16 log2 units (rescaled only in a
+//                 rare wave-uniform branch),
 //   O^T += V^T P^T (A = 16 dims x the lane group's 8 keys, B = the lane's 8
-//                 probabilities as bf16 hi + lo parts, so no lane exchange is
-//                 needed and the weights keep ~16 bits).
-// With one split the block finishes its rows itself; otherwise it writes
-// (max, sum, O) per row to the workspace and attn2_merge, one wave per
-// output row, combines the splits in split order, then applies the norm and
-// the gate.
+//                 weights as bf16 hi + lo parts, so no lane exchange is
+//                 needed and the weights keep ~16 bits); the row sums come
+//                 from the same parts through an all-ones A operand.
+// After the loop the 4 key groups merge in LDS.  With one split the block
+// finishes its rows itself; otherwise it writes (max, sum, O) per row to the
+// workspace and attn2_merge, one wave per output row, combines the splits in
+// split order, then applies the norm and the gate.
 #include <hip/hip_runtime.h>
 
 #include "qkvf_internal.h"

@@ -1,5 +1,7 @@
 // Internal interface between the C-ABI layer (qkvf_api.cpp) and the gfx950
-// kernels (qkvf_kernels.hip).  Not installed; the public API is include/qkvf.h.
+// kernels (the front in qkvf_kernels.hip, attn2 in qkvf_attn2.hip, LayerFront
+// in qkvf_layer_front.hip, MuseRouting in qkvf_route.hip).  Not installed; the
+// public API is include/qkvf.h.
 #pragma once
 
 #include <cstdint>
@@ -71,8 +73,8 @@ constexpr int kAttn2MaxReqs = 64;
 // max_model_len keys (window + 7 with a window); the keys are cut into about
 // kAttn2TargetBlocks / (num_reqs * nkv) splits so that a launch has ~256
 // blocks (one 16-wave block per CU), but no split is shorter than
-// kAttn2MinSplitKeys keys
-// (each split writes a 17 KB partial per KV head) and there are at most 64.
+// kAttn2MinSplitKeys keys (each split writes a 17 KB partial per KV head) and
+// there are at most 64.
 // The count depends on the deployment and the batch size, not on the step's
 // lengths, so the launch shape is fixed for a captured batch size; shorter
 // contexts leave the trailing splits empty.

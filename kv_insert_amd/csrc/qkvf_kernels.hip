@@ -34,8 +34,10 @@
 //
 //  No read-modify-write atomics, no flags to wait for and no cache
 //  maintenance: each partial travels with its call number in one 64-bit
-//  device-coherent (agent-scope) store, and a reader accepts a value only
-//  when its tag is the current call's.  The call number comes from a
+//  word, stored plainly into the XCD's L2 when its reader runs on the same
+//  XCD and written through (device-coherent, agent scope) otherwise; a
+//  reader's device-coherent loads accept a value only when its tag is the
+//  current call's.  The call number comes from a
 //  per-block counter that every call raises by one (so all counters agree at
 //  the start of a call, and a graph replay gets a new number).  The sums run
 //  in a fixed order, so the result depends on the launch shape only.
