@@ -45,17 +45,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef QKVF_ATTN2_GROUPS
-#define QKVF_ATTN2_GROUPS 4
-#endif
-#ifndef QKVF_ATTN2_DEPTH
-#define QKVF_ATTN2_DEPTH 2
-#endif
 constexpr int kChunk = 32;                     // keys of one MFMA pass (two pages)
-constexpr int kGroups = QKVF_ATTN2_GROUPS;     // key groups (chunks) per step
+constexpr int kGroups = 4;                     // key groups (chunks) per step
 constexpr int kStep = kChunk * kGroups;        // keys per step
 constexpr int kThreads = 256 * kGroups;        // 4 query waves per key group
-constexpr int kDepth = QKVF_ATTN2_DEPTH;       // steps of loads in flight
+constexpr int kDepth = 2;                      // steps of loads in flight
 // Page offsets are staged per segment of keys; a split of up to 4096 keys
 // (a 128K context over 32 splits) is one segment, so its ring never drains
 // for a restage.
