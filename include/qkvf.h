@@ -145,7 +145,8 @@ size_t qkvf_workspace_bytes(void);
  * default): a partial read on the XCD that produced it is stored plainly and
  * read from that XCD's L2, when qkvf_prepare found that the device places a
  * kernel's blocks on its 8 XCDs round robin (checked once per device with a
- * small kernel; if not, mode 1 is used).  mode 1: every partial is written through to memory.
+ * small kernel; if not, mode 1 is used).  mode 1: every partial is written
+ * through to memory.
  * Both modes give bitwise the same results; mode 1 is a little slower.  For
  * diagnostics and tests; applies to calls launched afterwards, process-wide.
  * Returns QKVF_OK, or QKVF_ERR_RANGE for another mode.
@@ -156,8 +157,9 @@ int qkvf_set_handoff(int mode);
  * Synchronize the current device and report whether any call on it since the
  * last query gave up waiting for a partial result (QKVF_ERR_TIMEOUT; the
  * outputs of that call are not valid).  Clears the record.  Returns QKVF_OK
- * when no call failed (or nothing was prepared on the device), QKVF_ERR_HIP
- * on a runtime error.
+ * when no call failed (or nothing was prepared on the device),
+ * QKVF_ERR_DEVICE when there is no current HIP device, QKVF_ERR_HIP on a
+ * runtime error.
  */
 int qkvf_device_fault(void);
 
