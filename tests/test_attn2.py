@@ -142,6 +142,23 @@ def test_attn2_max_requests():
     case.oracle_check(to_bits(run_attn2(case, b.name)))
 
 
+@pytest.mark.parametrize("nkv,mml,lens,window", [(2, 2048, (8, 100, 2048), 0),
+                                                 (8, 32768, (5000,), 0),
+                                                 (4, 8192, (3000, 777), 100)])
+def test_attn2_small_values_where_eps_matters(nkv, mml, lens, window):
+    """Values of ~2e-3 put mean(o^2) near the o-norm's eps: only there do the
+    softmax sums and eps change the output (the weightless RMS norm cancels
+    any other scale of o), so this checks the kernel's row sums and the
+    merge's weighting of the splits, which unit-scale values cannot."""
+    a = wl.Attn2Workload(f"small_v_nkv{nkv}", nkv=nkv, max_model_len=mml, lens=lens,
+                         window=window, index=50 + nkv)
+    case = Attn2Case(a)
+    c = case.cache.float()
+    c[..., 64:] *= 2e-3
+    case.cache = c.to(torch.bfloat16)
+    case.oracle_check(to_bits(run_attn2(case, a.name)))
+
+
 def shared_page_case(a: wl.Attn2Workload, seed: int) -> Attn2Case:
     """An Attn2Case whose requests all read one set of pages (enough for
     max_model_len), each through its own random permutation of the block

@@ -21,13 +21,15 @@ def bits(a):
             .view(torch.int16).numpy().view(np.uint16))
 
 
-def rand_case(rng, R, nkv, Ls, pages=None, scale_q=1.0):
+def rand_case(rng, R, nkv, Ls, pages=None, scale_q=1.0, scale_v=1.0):
     nq = 8 * nkv
     max_pages = max((L + 15) // 16 for L in Ls)
     pages = pages or R * max_pages + 3
     q = bits(rng.standard_normal((R * 8, nq * 64)) * scale_q)
     gate = bits(rng.standard_normal((R * 8, nq * 64)))
-    cache = bits(rng.standard_normal((pages, nkv, 16, 128)))
+    c = rng.standard_normal((pages, nkv, 16, 128))
+    c[..., 64:] *= scale_v
+    cache = bits(c)
     perm = rng.permutation(pages)
     bt = np.zeros((R, max_pages), np.int32)
     for r in range(R):
@@ -78,6 +80,21 @@ def test_attn2_matches_float64_torch(nkv, Ls, window):
     # both round the same double value to bf16; allow one unit where the
     # double results straddle a rounding midpoint
     g = oracle.bf16_to_float(got)
+    assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-30)
+
+
+@pytest.mark.parametrize("Ls,window", [([8, 37, 100], 0), ([50, 129], 16)])
+def test_attn2_small_values_where_eps_matters(Ls, window):
+    """Values of ~2e-3 put mean(o^2) near eps = 1e-6: only there do the
+    softmax normalisation and eps change the normed output (the weightless
+    RMS norm cancels any other scale of o), so a dropped normalisation or a
+    dropped eps shows here and nowhere else."""
+    rng = np.random.default_rng(300 + len(Ls) + window)
+    q, gate, cache, bt, sl = rand_case(rng, len(Ls), 1, Ls, scale_v=2e-3)
+    ref = dense_reference(q, gate, cache, 1, bt, sl, window)
+    v = oracle.bf16_to_float(cache)[..., 64:]
+    assert 1e-8 < float(np.mean(v * v)) < 1e-4
+    g = oracle.bf16_to_float(oracle.attn2(q, gate, cache, 1, bt, sl, window))
     assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-30)
 
 

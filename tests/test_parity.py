@@ -94,6 +94,17 @@ def test_zero_token_rows_give_zero_heads():
     assert torch.isfinite(y).all()
 
 
+def test_small_rows_where_eps_matters():
+    """Rows scaled by 1e-2 down to 3e-5 put the heads' mean square near the
+    norm's eps = 1e-6, the only place where eps changes the normed q and k
+    heads (at unit scale it cannot be seen)."""
+    case = Case(wl.C2)
+    scales = torch.tensor([1e-3, 3e-4, 1e-4, 3e-5, 1.0, 1e-2, 3e-3, 1e-3])
+    case.x = (case.x.float() * scales[:, None]).to(torch.bfloat16)
+    g = run_gpu(case, label="small rows")
+    check(case, g)
+
+
 def test_exact_integer_inputs_are_bit_exact():
     """x, W in {-1, 0, 1}: every fp32 summation order is exact, so the
     projection (v and gate columns, V in the cache) must match bit for bit."""
