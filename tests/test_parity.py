@@ -121,6 +121,30 @@ def test_exact_integer_inputs_are_bit_exact():
     assert torch.equal(y[:, qk:], z[:, qk:].to(torch.bfloat16).double())
 
 
+def test_exact_integer_rounding_is_nearest_even_with_ties():
+    """x in {0, 1} and W rows of +-{0, 1} at half density: every fp32
+    summation order is still exact, but |z| sits around 2048, where bf16's
+    spacing is 8 below and 16 above, so most values round and one in eight
+    or sixteen is an exact tie.  The v and gate columns must equal the
+    exact sums rounded to nearest, ties to even, bit for bit."""
+    w = wl.sweep(8, 2)
+    rng = np.random.default_rng(78)
+    case = Case(w)
+    case.x = torch.from_numpy(rng.choice([0.0, 1.0], size=(8, 8192)).astype(np.float32)).to(torch.bfloat16)
+    sign = rng.choice([-1.0, 1.0], size=(w.N, 1))
+    case.W = torch.from_numpy((rng.choice([0.0, 1.0], size=(w.N, 8192)) * sign).astype(np.float32)).to(torch.bfloat16)
+    z = case.x.double() @ case.W.double().T
+    qk = (8 * w.nkv + w.nkv) * 64
+    zt = z[:, qk:]
+    assert zt.abs().min() > 1024 and zt.abs().max() < 4096
+    ties = ((zt.abs() - 1024) % 8 == 4) & (zt.abs() < 2048) | ((zt.abs() - 2048) % 16 == 8) & (zt.abs() >= 2048)
+    assert int(ties.sum()) > 100
+    g = run_gpu(case, label="integer rounding and ties")
+    check(case, g)
+    y = g["y"].double().cpu()
+    assert torch.equal(y[:, qk:], zt.to(torch.bfloat16).double())
+
+
 def test_rows_past_M_and_neighbours_untouched():
     w = wl.C4
     case = Case(w, M=5)
