@@ -182,7 +182,8 @@ int qkvf_device_fault(void);
  * calls split their keys over several blocks (the split count depends on
  * these values and the call's request count only, see qkvf_attn2_plan, so
  * the launch shape of a batch size is fixed and capturable).  It may
- * allocate and synchronize; no attn2 call may be in flight.
+ * allocate; a workspace it outgrows stays allocated (a call already
+ * launched may still use it) until qkvf_release.
  * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS (max_reqs outside [1, 64]),
  * QKVF_ERR_DEVICE, QKVF_ERR_ALLOC.
  */
@@ -277,8 +278,9 @@ int qkvf_route(const float *logits, int64_t logits_row_stride, const float *bias
                double route_scale, int num_tokens, int32_t *ids, float *weights,
                hipStream_t stream);
 
-/* Free the workspace of every device and forget prepared shapes.  No call
- * may be in flight. */
+/* Synchronize each device that holds a workspace, free every workspace of
+ * the library and forget prepared shapes.  No call may be made concurrently
+ * from another thread. */
 void qkvf_release(void);
 
 #ifdef __cplusplus

@@ -6,6 +6,7 @@
 #include "qkvf.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -21,18 +22,26 @@ using namespace qkvf;
 
 constexpr int kMaxDevices = 64;
 
+// Per-device state.  Writers hold g_mu; the launch entries read the atomic
+// fields without it: a workspace is published (release) only once it is
+// initialised, and a row count is marked prepared only after that.
 struct DeviceState {
-    float *ws = nullptr;
-    float *attn2_ws = nullptr;        // split partials of attn2
-    size_t attn2_ws_floats = 0;
-    int arch_ok = -1;                 // -1 unknown, 0 not gfx950, 1 gfx950
-    bool round_robin = false;         // blocks with equal b % 8 verified to share an XCD
-    unsigned prepared[9] = {};        // per nkv: bit m set once rows m are prepared
+    std::atomic<float *> ws{nullptr};
+    std::atomic<bool> round_robin{false};     // blocks with equal b % 8 verified to share an XCD
+    std::atomic<unsigned> prepared[9] = {};   // per nkv: bit m set once rows m are prepared
+    // Split partials of attn2.  A larger workspace is published before its
+    // size, so a reader that sees the size also sees a buffer of that size;
+    // a replaced one is kept (a call on another thread may still use it)
+    // until qkvf_release.
+    std::atomic<float *> attn2_ws{nullptr};
+    std::atomic<size_t> attn2_ws_floats{0};
+    std::vector<float *> retired;
+    int arch_ok = -1;                         // -1 unknown, 0 not gfx950, 1 gfx950
 };
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
-bool g_force_coherent = false;        // qkvf_set_handoff(1)
+std::atomic<bool> g_force_coherent{false};    // qkvf_set_handoff(1)
 
 // Shape bound by the last qkvf_prepare of this thread.
 thread_local int t_N = 0;
@@ -60,7 +69,7 @@ int shape_status(int N, int nkv, int M)
     return QKVF_OK;
 }
 
-// Current device index, with its gfx950 check cached.  Locks g_mu.
+// Current device index, with its gfx950 check cached.  The caller holds g_mu.
 int current_device(int *dev_out)
 {
     int count = 0;
@@ -128,7 +137,7 @@ int qkvf_prepare(int N, int num_kv_heads, int M)
         (void)hipGetLastError();
         return QKVF_ERR_DEVICE;
     }
-    if (st.ws == nullptr) {
+    if (st.ws.load(std::memory_order_relaxed) == nullptr) {
         void *p = nullptr;
         if (hipMalloc(&p, kWorkspaceFloats * sizeof(float)) != hipSuccess) {
             (void)hipGetLastError();
@@ -141,19 +150,19 @@ int qkvf_prepare(int N, int num_kv_heads, int M)
             (void)hipFree(p);
             return QKVF_ERR_HIP;
         }
-        st.ws = static_cast<float *>(p);
         // Where do the kernel's blocks run?  If round robin over the XCDs,
         // blocks with equal b % 8 share an XCD, and a partial read by one of
         // them may stay in that XCD's L2.
         bool rr = false;
-        if (check_placement(reinterpret_cast<unsigned *>(st.ws) + kPlacementOffset, &rr) !=
-            hipSuccess) {
+        if (check_placement(static_cast<unsigned *>(p) + kPlacementOffset, &rr) != hipSuccess) {
             (void)hipGetLastError();
+            (void)hipFree(p);
             return QKVF_ERR_HIP;
         }
-        st.round_robin = rr;
+        st.round_robin.store(rr, std::memory_order_relaxed);
+        st.ws.store(static_cast<float *>(p), std::memory_order_release);
     }
-    st.prepared[num_kv_heads] |= (2u << M) - 2u;  // rows 1..M
+    st.prepared[num_kv_heads].fetch_or((2u << M) - 2u, std::memory_order_release);  // rows 1..M
     t_N = N;
     t_nkv = num_kv_heads;
     return QKVF_OK;
@@ -175,11 +184,15 @@ int qkvf_run(const void *x, const void *W, const int64_t *positions, const int64
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QKVF_ERR_DEVICE;
     const DeviceState &st = g_dev[dev];
-    if (st.ws == nullptr || !(st.prepared[t_nkv] & (1u << M)))
+    if (!(st.prepared[t_nkv].load(std::memory_order_acquire) & (1u << M)))
         return QKVF_ERR_NOT_PREPARED;
-    const bool coherent = g_force_coherent || !st.round_robin;
+    float *ws = st.ws.load(std::memory_order_acquire);
+    if (ws == nullptr)   // released meanwhile
+        return QKVF_ERR_NOT_PREPARED;
+    const bool coherent = g_force_coherent.load(std::memory_order_relaxed) ||
+                          !st.round_robin.load(std::memory_order_relaxed);
     const hipError_t e = launch_front(t_nkv, M, x, W, positions, slots, cos_sin, y, kv_cache,
-                                      st.ws, coherent, stream);
+                                      ws, coherent, stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }
 
@@ -290,8 +303,7 @@ int qkvf_set_handoff(int mode)
 {
     if (mode != 0 && mode != 1)
         return QKVF_ERR_RANGE;
-    std::lock_guard<std::mutex> lock(g_mu);
-    g_force_coherent = mode == 1;
+    g_force_coherent.store(mode == 1, std::memory_order_relaxed);
     return QKVF_OK;
 }
 
@@ -301,11 +313,11 @@ int qkvf_device_fault(void)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QKVF_ERR_DEVICE;
-    DeviceState &st = g_dev[dev];
-    if (st.ws == nullptr)
+    float *ws = g_dev[dev].ws.load(std::memory_order_acquire);
+    if (ws == nullptr)
         return QKVF_OK;
     unsigned word = 0;
-    unsigned *fault = reinterpret_cast<unsigned *>(st.ws) + kFaultWord;
+    unsigned *fault = reinterpret_cast<unsigned *>(ws) + kFaultWord;
     if (hipDeviceSynchronize() != hipSuccess ||
         hipMemcpy(&word, fault, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) {
         (void)hipGetLastError();
@@ -328,14 +340,24 @@ void qkvf_release(void)
     (void)hipGetDevice(&cur);
     for (int d = 0; d < kMaxDevices; ++d) {
         DeviceState &st = g_dev[d];
-        if (st.ws != nullptr || st.attn2_ws != nullptr) {
+        for (auto &bits : st.prepared)   // first, so no launch starts on a freed workspace
+            bits.store(0);
+        float *ws = st.ws.exchange(nullptr);
+        float *aws = st.attn2_ws.exchange(nullptr);
+        st.attn2_ws_floats.store(0);
+        if (ws != nullptr || aws != nullptr || !st.retired.empty()) {
             (void)hipSetDevice(d);
-            if (st.ws != nullptr)
-                (void)hipFree(st.ws);
-            if (st.attn2_ws != nullptr)
-                (void)hipFree(st.attn2_ws);
+            (void)hipDeviceSynchronize();
+            if (ws != nullptr)
+                (void)hipFree(ws);
+            if (aws != nullptr)
+                (void)hipFree(aws);
+            for (float *r : st.retired)
+                (void)hipFree(r);
         }
-        st = DeviceState{};
+        st.retired.clear();
+        st.round_robin.store(false);
+        st.arch_ok = -1;
     }
     if (cur >= 0)
         (void)hipSetDevice(cur);
@@ -359,18 +381,16 @@ int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int wi
     // A window that covers every position is no window.
     const int win = window >= max_model_len ? 0 : window;
     const size_t need = attn2_workspace_floats(num_kv_heads, max_reqs, max_model_len, win);
-    if (need > st.attn2_ws_floats) {
+    if (need > st.attn2_ws_floats.load(std::memory_order_relaxed)) {
         void *p = nullptr;
         if (hipMalloc(&p, need * sizeof(float)) != hipSuccess) {
             (void)hipGetLastError();
             return QKVF_ERR_ALLOC;
         }
-        if (st.attn2_ws != nullptr) {
-            (void)hipDeviceSynchronize();
-            (void)hipFree(st.attn2_ws);
-        }
-        st.attn2_ws = static_cast<float *>(p);
-        st.attn2_ws_floats = need;
+        float *old = st.attn2_ws.exchange(static_cast<float *>(p), std::memory_order_release);
+        st.attn2_ws_floats.store(need, std::memory_order_release);
+        if (old != nullptr)
+            st.retired.push_back(old);
     }
     t_attn2 = Attn2Config{num_kv_heads, max_model_len, max_reqs, win};
     return QKVF_OK;
@@ -402,11 +422,13 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate, int64_
     const DeviceState &st = g_dev[dev];
     const int z = attn2_splits(cfg.nkv, num_reqs, cfg.max_model_len, cfg.window);
     const size_t need = z > 1 ? size_t(num_reqs) * cfg.nkv * z * 64 * kAttn2PartialFloats : 0;
-    if (need > st.attn2_ws_floats)
+    // Size first: a buffer published with this size or a later, larger one.
+    if (need > st.attn2_ws_floats.load(std::memory_order_acquire))
         return QKVF_ERR_NOT_PREPARED;
+    float *ws = st.attn2_ws.load(std::memory_order_acquire);
     const hipError_t e = launch_attn2(q, q_row_stride, gate, gate_row_stride, kv_cache, cfg.nkv,
                                       block_table, block_table_stride, seq_lens, num_reqs,
-                                      cfg.max_model_len, cfg.window, z, st.attn2_ws, out, out_row_stride,
+                                      cfg.max_model_len, cfg.window, z, ws, out, out_row_stride,
                                       stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }
