@@ -1,7 +1,9 @@
 """bench.py's contract that runs without a GPU: more than one GPU is refused
 with a message before anything touches a device, unknown workloads are
-refused, and the workloads' algorithmic byte counts are the documented
-formulas at the documented sizes."""
+refused, the workloads' algorithmic byte counts are the documented
+formulas at the documented sizes, and counter traffic is reported only for
+the kernel source it was measured on."""
+import json
 import os
 import subprocess
 import sys
@@ -9,6 +11,8 @@ import sys
 from kv_insert_amd import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
 
 
 def run_bench(*args):
@@ -47,3 +51,33 @@ def test_layer_front_and_route_bytes():
     assert wl.LF1.algorithmic_bytes() == 16 * 8192 * (2 + 8 + 2) + 2 * 8192
     assert wl.LF2.algorithmic_bytes() == 8 * 8192 * (4 + 4 + 2) + 2 * 8192
     assert wl.RT1.algorithmic_bytes() == 8 * 256 * 4 + 256 * 4 + 2 * 8 * 8 * 4
+
+
+def test_traffic_is_reported_only_for_the_kernel_it_was_measured_on(tmp_path):
+    """bench.py reports a counter record's HBM bytes only while the kernel
+    source still has the hash the record was taken on."""
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel v1\n")
+    rec = tmp_path / "counters.json"
+    w = wl.C3
+    rec.write_text(json.dumps({"kernel_sha256_16": bench.kernel_hash(str(src)),
+                               "workloads": {w.name: {"hbm_bytes_per_launch": 123}}}))
+    assert bench.measured_traffic(w, str(rec), str(src)) == 123
+    assert bench.measured_traffic(wl.C4, str(rec), str(src)) is None      # no entry
+    src.write_text("// kernel v2\n")
+    assert bench.measured_traffic(w, str(rec), str(src)) is None          # source changed
+    assert bench.measured_traffic(w, str(tmp_path / "missing.json"), str(src)) is None
+
+
+def test_committed_counter_records_have_their_fields():
+    """Each record in profiles/ names the hash it was taken on and gives HBM
+    bytes per call for workloads bench.py knows."""
+    for path, table in ((bench.COUNTERS, wl.WORKLOADS), (bench.ATTN2_COUNTERS, wl.ATTN2_WORKLOADS),
+                        (bench.LF_COUNTERS, wl.LAYER_FRONT_WORKLOADS)):
+        rec = json.load(open(path))
+        assert len(rec["kernel_sha256_16"]) == 16
+        assert rec["workloads"]
+        for name, entry in rec["workloads"].items():
+            assert name in table
+            b = entry.get("hbm_bytes_per_launch", entry.get("hbm_bytes_per_call"))
+            assert b > table[name].algorithmic_bytes() * 0.9
