@@ -280,6 +280,47 @@ def attn2_line(a: wl.Attn2Workload, args) -> dict:
     }
 
 
+def graph_rotation_time(call, sets: int, steps: int, warmup: int, repeats: int, stream):
+    """Per-call time of a launch-bound kernel: one rotation of `sets` calls
+    is captured in a HIP graph and replayed until about `steps` calls have
+    run (the way such calls run in a decode step; issued one by one from
+    Python, the host's enqueue rate would be measured instead).  Also
+    returns the eager per-call time of 500 calls, for context."""
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, sets)):
+            call(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    with torch.cuda.stream(stream):
+        for i in range(500):
+            call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / 500
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(sets):
+            call(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    replays = max(1, steps // sets)
+    times = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(replays):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / (replays * sets))
+    return sorted(times)[len(times) // 2], times, replays * sets, eager_ms
+
+
 def time_layer_front(w: wl.LayerFrontWorkload, steps: int, warmup: int, repeats: int):
     """Calls rotate over input/output sets of >= 600 MB in total, so every
     call's rows come from HBM."""
@@ -301,22 +342,8 @@ def time_layer_front(w: wl.LayerFrontWorkload, steps: int, warmup: int, repeats:
         qf.layer_front(xs[s], st[s], out[s], aux=None if ax is None else ax[s], weight=weight,
                        stream=stream)
 
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            call(i)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(repeats):
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(steps):
-            call(warmup + i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        times.append(start.elapsed_time(end) / steps)
-    return sorted(times)[len(times) // 2], times, sets
+    ms, times, calls, eager_ms = graph_rotation_time(call, sets, steps, warmup, repeats, stream)
+    return ms, times, sets, calls, eager_ms
 
 
 def layer_front_cpu_baseline(w: wl.LayerFrontWorkload, budget_s: float) -> dict | None:
@@ -342,17 +369,19 @@ def layer_front_cpu_baseline(w: wl.LayerFrontWorkload, budget_s: float) -> dict 
 
 
 def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
-    ms, times, sets = time_layer_front(w, args.steps, args.warmup, args.repeats)
+    ms, times, sets, calls, eager_ms = time_layer_front(w, args.steps, args.warmup, args.repeats)
     nbytes = w.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {
         "metric": "LayerFront achieved HBM GB/s (algorithmic bytes per call / time per call)",
-        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": calls,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if w.fp32_input else "bf16", "data": "synthetic",
         "config": dict(wl.describe_layer_front(w), sets_rotated=sets,
-                       algorithmic_bytes_per_call=nbytes),
+                       algorithmic_bytes_per_call=nbytes,
+                       timing=f"one rotation of {sets} calls captured in a HIP graph and replayed",
+                       eager_us_per_call=round(eager_ms * 1e3, 3)),
         "roofline": {"bound": "hbm", "kernel": "layer_front (the whole call)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -362,7 +391,8 @@ def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
 
 
 def route_line(w: wl.RouteWorkload, args) -> dict:
-    """MuseRouting calls rotate over 64 input sets (the data are a few KB)."""
+    """MuseRouting calls rotate over 64 input sets (the data are a few KB),
+    timed by graph replay like LayerFront's."""
     dev = "cuda"
     sets = 64
     inputs = [wl.make_route_inputs(w, s, device=dev) for s in range(sets)]
@@ -374,22 +404,8 @@ def route_line(w: wl.RouteWorkload, args) -> dict:
         s = i % sets
         qf.route(inputs[s][0], inputs[s][1], w.route_scale, ids[s], wts[s], stream=stream)
 
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            call(i)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(args.repeats):
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(args.steps):
-            call(args.warmup + i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        times.append(start.elapsed_time(end) / args.steps)
-    ms = sorted(times)[len(times) // 2]
+    ms, times, calls, eager_ms = graph_rotation_time(call, sets, args.steps, args.warmup,
+                                                     args.repeats, stream)
     nbytes = w.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     base = None
@@ -397,22 +413,24 @@ def route_line(w: wl.RouteWorkload, args) -> dict:
         import oracle
         lg, bs = wl.make_route_inputs(w, 0)
         lg, bs = lg.numpy(), bs.numpy()
-        calls, t0 = 0, time.perf_counter()
+        ncalls, t0 = 0, time.perf_counter()
         while time.perf_counter() - t0 < min(args.cpu_baseline_seconds, 2.0):
             oracle.route(lg, bs, w.route_scale)
-            calls += 1
-        per = (time.perf_counter() - t0) / calls
+            ncalls += 1
+        per = (time.perf_counter() - t0) / ncalls
         base = {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s",
                 "us_per_call": round(per * 1e6, 2), "cores": 1, "kind": "oracle",
-                "sample": f"{calls} full oracle calls of {w.name} (input set 0), one thread"}
+                "sample": f"{ncalls} full oracle calls of {w.name} (input set 0), one thread"}
     return {
         "metric": "MuseRouting us per call (and algorithmic GB/s)",
-        "value": round(gbs, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(gbs, 3), "unit": "GB/s", "n_gpus": 1, "steps": calls,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "experts": 256, "top_k": 8,
-                   "route_scale": w.route_scale, "algorithmic_bytes_per_call": nbytes},
+                   "route_scale": w.route_scale, "algorithmic_bytes_per_call": nbytes,
+                   "timing": f"one rotation of {sets} calls captured in a HIP graph and replayed",
+                   "eager_us_per_call": round(eager_ms * 1e3, 3)},
         "roofline": {"bound": "hbm", "kernel": "route (the whole call)", "achieved": round(gbs, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6),
                      "traffic": None},

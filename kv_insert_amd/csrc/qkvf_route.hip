@@ -10,7 +10,8 @@
 //                                           rounded once to fp32
 // One wave per token; lane l holds experts 4 l .. 4 l + 3.  Each of the 8
 // selection rounds takes a wave-wide max over 64-bit values that order by
-// key and then by lower id, so the ranking needs no data-dependent branch.
+// key and then by lower id, so the ranking needs no data-dependent branch;
+// the maximum moves between lanes by DPP, not through the LDS crossbar.
 #include <hip/hip_runtime.h>
 
 #include "qkvf_internal.h"
@@ -28,14 +29,32 @@ __device__ inline uint32_t ordered(float f)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// One step of a wave-wide 64-bit max: combine v with the value the DPP
+// pattern CTRL brings from another lane (rows outside ROW_MASK keep v).
+template <int CTRL, int ROW_MASK>
+__device__ inline uint64_t max_dpp(uint64_t v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(int(uint32_t(v)), int(uint32_t(v)), CTRL, ROW_MASK,
+                                               0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(int(uint32_t(v >> 32)), int(uint32_t(v >> 32)),
+                                               CTRL, ROW_MASK, 0xf, false);
+    const uint64_t o = (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+    return o > v ? o : v;
+}
+
+// The wave-wide maximum, in every lane: lane swaps within quads, mirrors
+// within 8 and 16 lanes, then row broadcasts carry the maximum to lane 63.
 __device__ inline uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) {
-        const uint64_t o = __shfl_xor(v, k, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max_dpp<0xb1, 0xf>(v);    // quad_perm [1, 0, 3, 2]
+    v = max_dpp<0x4e, 0xf>(v);    // quad_perm [2, 3, 0, 1]
+    v = max_dpp<0x141, 0xf>(v);   // row_half_mirror
+    v = max_dpp<0x140, 0xf>(v);   // row_mirror: every lane holds its row's max
+    v = max_dpp<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v = max_dpp<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3: lane 63 holds the max
+    const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(v)), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63);
+    return (uint64_t(hi) << 32) | lo;
 }
 
 __global__ void __launch_bounds__(64)
@@ -70,7 +89,7 @@ route(const float *__restrict__ logits, int64_t row_stride, const float *__restr
         if ((e >> 2) == lane)
             cand[e & 3] = 0;
         const float mine = score[e & 3];
-        chosen[k] = __shfl(mine, e >> 2, 64);
+        chosen[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e >> 2));
         pick[k] = e;
     }
     double sum = 0.0;
