@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--route", default="", metavar="WORKLOAD",
                     help="time MuseRouting instead of the front: one of "
                          + ", ".join(wl.ROUTE_WORKLOADS))
+    ap.add_argument("--eager", action="store_true",
+                    help="time LayerFront and routing calls issued one by one instead of "
+                         "replaying a HIP graph (for profiler runs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="instead of the front, time device-to-device copies of MB megabytes "
                          "(a plain copy kernel of known size, for scaling memory counters)")
@@ -280,12 +283,39 @@ def attn2_line(a: wl.Attn2Workload, args) -> dict:
     }
 
 
-def graph_rotation_time(call, sets: int, steps: int, warmup: int, repeats: int, stream):
+def eager_time(call, steps: int, warmup: int, repeats: int, stream):
+    """Per-call time of `steps` calls issued one by one after `warmup`."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                call(warmup + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / steps)
+    return sorted(times)[len(times) // 2], times
+
+
+def graph_rotation_time(call, sets: int, steps: int, warmup: int, repeats: int, stream,
+                        eager: bool = False):
     """Per-call time of a launch-bound kernel: one rotation of `sets` calls
     is captured in a HIP graph and replayed until about `steps` calls have
     run (the way such calls run in a decode step; issued one by one from
     Python, the host's enqueue rate would be measured instead).  Also
-    returns the eager per-call time of 500 calls, for context."""
+    returns the eager per-call time of 500 calls, for context.  With
+    eager=True only `warmup` + `steps` calls are issued one by one (for
+    profiler runs, where each dispatch is slow)."""
+    if eager:
+        ms, times = eager_time(call, steps, warmup, repeats, stream)
+        return ms, times, steps, ms
     with torch.cuda.stream(stream):
         for i in range(max(warmup, sets)):
             call(i)
@@ -321,7 +351,8 @@ def graph_rotation_time(call, sets: int, steps: int, warmup: int, repeats: int, 
     return sorted(times)[len(times) // 2], times, replays * sets, eager_ms
 
 
-def time_layer_front(w: wl.LayerFrontWorkload, steps: int, warmup: int, repeats: int):
+def time_layer_front(w: wl.LayerFrontWorkload, steps: int, warmup: int, repeats: int,
+                     eager: bool = False):
     """Calls rotate over input/output sets of >= 600 MB in total, so every
     call's rows come from HBM."""
     dev = "cuda"
@@ -342,7 +373,8 @@ def time_layer_front(w: wl.LayerFrontWorkload, steps: int, warmup: int, repeats:
         qf.layer_front(xs[s], st[s], out[s], aux=None if ax is None else ax[s], weight=weight,
                        stream=stream)
 
-    ms, times, calls, eager_ms = graph_rotation_time(call, sets, steps, warmup, repeats, stream)
+    ms, times, calls, eager_ms = graph_rotation_time(call, sets, steps, warmup, repeats, stream,
+                                                     eager)
     return ms, times, sets, calls, eager_ms
 
 
@@ -369,7 +401,8 @@ def layer_front_cpu_baseline(w: wl.LayerFrontWorkload, budget_s: float) -> dict 
 
 
 def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
-    ms, times, sets, calls, eager_ms = time_layer_front(w, args.steps, args.warmup, args.repeats)
+    ms, times, sets, calls, eager_ms = time_layer_front(w, args.steps, args.warmup, args.repeats,
+                                                        args.eager)
     nbytes = w.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {
@@ -380,7 +413,8 @@ def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
         "dtype": "f32" if w.fp32_input else "bf16", "data": "synthetic",
         "config": dict(wl.describe_layer_front(w), sets_rotated=sets,
                        algorithmic_bytes_per_call=nbytes,
-                       timing=f"one rotation of {sets} calls captured in a HIP graph and replayed",
+                       timing="calls issued one by one" if args.eager else
+                       f"one rotation of {sets} calls captured in a HIP graph and replayed",
                        eager_us_per_call=round(eager_ms * 1e3, 3)),
         "roofline": {"bound": "hbm", "kernel": "layer_front (the whole call)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -405,7 +439,7 @@ def route_line(w: wl.RouteWorkload, args) -> dict:
         qf.route(inputs[s][0], inputs[s][1], w.route_scale, ids[s], wts[s], stream=stream)
 
     ms, times, calls, eager_ms = graph_rotation_time(call, sets, args.steps, args.warmup,
-                                                     args.repeats, stream)
+                                                     args.repeats, stream, args.eager)
     nbytes = w.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     base = None
@@ -429,7 +463,8 @@ def route_line(w: wl.RouteWorkload, args) -> dict:
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "experts": 256, "top_k": 8,
                    "route_scale": w.route_scale, "algorithmic_bytes_per_call": nbytes,
-                   "timing": f"one rotation of {sets} calls captured in a HIP graph and replayed",
+                   "timing": "calls issued one by one" if args.eager else
+                   f"one rotation of {sets} calls captured in a HIP graph and replayed",
                    "eager_us_per_call": round(eager_ms * 1e3, 3)},
         "roofline": {"bound": "hbm", "kernel": "route (the whole call)", "achieved": round(gbs, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6),
