@@ -503,7 +503,8 @@ def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU (asked for {a.gpus}); the front is a "
-              "single-GPU kernel (sharding by KV heads is described in DESIGN.md)",
+              "single-GPU kernel: several GPUs would each run it on their own KV heads' share "
+              "of the weights and cache, with no traffic between them",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
