@@ -100,7 +100,12 @@ int qkvf_prepare(int N, int num_kv_heads, int M);
  * stream, or streams ordered by events) and not overlap other calls of this
  * library on the device.  A call that cannot make progress (calls
  * overlapped) gives up after a bounded wait, leaves invalid outputs and
- * records a fault that qkvf_device_fault reports.
+ * records a fault that qkvf_device_fault reports.  Partials pass between
+ * blocks tagged with a 32-bit call number: a stale partial could be taken
+ * only if its workspace position was last written a whole multiple of 2^32
+ * calls earlier (a position unused for 2^32 calls, then used again);
+ * qkvf_release followed by qkvf_prepare zeroes the workspace and restarts
+ * the count.
  * Errors (cheap scalar checks only): QKVF_ERR_NOT_PREPARED, QKVF_ERR_ROWS,
  * QKVF_ERR_NULLPTR, QKVF_ERR_ALIGN, QKVF_ERR_DEVICE, QKVF_ERR_HIP.
  */
