@@ -223,7 +223,7 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate,
 
 /* The number of key splits attn2 uses for a layer and a request count: about
  * 256 / (num_reqs * num_kv_heads) blocks per request and KV head, at most
- * one per 256 keys of the span a request's rows attend (max_model_len, or
+ * one per 128 keys of the span a request's rows attend (max_model_len, or
  * window + 7), at most 64; 1 means no merge pass.  A pure function of its
  * arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or QKVF_ERR_ROWS. */
 int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_reqs,

@@ -79,7 +79,7 @@ constexpr int kAttn2MaxReqs = 64;
 // lengths, so the launch shape is fixed for a captured batch size; shorter
 // contexts leave the trailing splits empty.
 constexpr int kAttn2TargetBlocks = 256;
-constexpr int kAttn2MinSplitKeys = 256;
+constexpr int kAttn2MinSplitKeys = 128;
 constexpr int kAttn2MaxSplits = 64;
 
 inline int attn2_span(int max_model_len, int window)

@@ -136,14 +136,15 @@ def test_no_device_here_means_device_error(L):
 
 
 @pytest.mark.parametrize("nkv,mml,window,reqs,splits", [
-    (8, 131072, 0, 1, 32), (8, 32768, 0, 2, 16), (1, 131072, 0, 1, 64), (2, 4096, 0, 1, 16),
-    (4, 8192, 0, 3, 22), (8, 2048, 0, 1, 8), (8, 256, 0, 1, 1), (8, 257, 0, 1, 2),
-    (8, 131072, 4096, 2, 16), (8, 131072, 4096, 1, 17), (2, 2048, 4096, 1, 8),
+    (8, 131072, 0, 1, 32), (8, 32768, 0, 2, 16), (1, 131072, 0, 1, 64), (2, 4096, 0, 1, 32),
+    (4, 8192, 0, 3, 22), (8, 2048, 0, 1, 16), (8, 128, 0, 1, 1), (8, 129, 0, 1, 2),
+    (8, 256, 0, 1, 2), (8, 257, 0, 1, 3), (8, 131072, 4096, 2, 16), (8, 131072, 4096, 1, 32),
+    (8, 131072, 8192, 1, 32), (2, 2048, 4096, 1, 16),
     (1, 8, 0, 1, 1), (8, 131072, 0, 64, 1), (8, 131072, 0, 40, 1), (1, 2048, 1, 1, 1),
     (2, 131072, 0, 40, 4),
 ])
 def test_attn2_plan(L, nkv, mml, window, reqs, splits):
-    """Split count: ceil(256 / (reqs nkv)) capped by one split per 256 keys of
+    """Split count: ceil(256 / (reqs nkv)) capped by one split per 128 keys of
     the span (max_model_len, or window + 7) and by 64; 1 below 2."""
     import ctypes
     z = ctypes.c_int(-1)
