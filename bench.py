@@ -147,6 +147,39 @@ def cpu_baseline(w: wl.Workload, budget_s: float) -> dict | None:
             "sample": f"{calls} full oracle calls of {w.name} (weight set 0), {threads} OpenMP threads"}
 
 
+def stream_context(w: wl.Workload, sets: int, steps: int, repeats: int) -> dict:
+    """For context: qkvf_stream_read (a plain streaming read with the front's
+    launch and load shape) over buffers the size of one weight set, rotated
+    over as many sets as the front's timing, timed the same way."""
+    nbytes = w.N * wl.HIDDEN * 2
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(sets)]
+    sink = torch.empty(256 * 512, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(2 * sets):
+            qf.stream_read(bufs[i % sets], sink, stream)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            qf.stream_read(bufs[i % sets], sink, stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / steps)
+    ms = sorted(times)[len(times) // 2]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "qkvf_stream_read (plain streaming read, 256 x 512 threads, "
+                      "8 x 16-byte non-temporal loads in flight per lane)",
+            "bytes_per_call": nbytes, "buffers_rotated": sets,
+            "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(gbs, 1),
+            "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def time_front(w: wl.Workload, sets: int, steps: int, warmup: int, repeats: int):
     pool = Pool(w, sets)
     qf.prepare(w.N, w.nkv, w.M)
@@ -567,6 +600,7 @@ def main():
                   file=sys.stderr, flush=True)
     base = cpu_baseline(w, a.cpu_baseline_seconds)
     traffic = measured_traffic(w)
+    context = stream_context(w, sets, a.steps, a.repeats)
     out = {
         "metric": "QKV-front achieved HBM GB/s (algorithmic bytes per call / time per call); "
                   "us_per_call alongside, fraction of peak in roofline.frac",
@@ -589,6 +623,7 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(traffic)},
         "cpu_baseline": base,
+        "stream_context": context,
         "repeats_ms": [round(t, 6) for t in times],
     }
     print(json.dumps(out), flush=True)

@@ -283,6 +283,23 @@ int qkvf_route(const float *logits, int64_t logits_row_stride, const float *bias
                double route_scale, int num_tokens, int32_t *ids, float *weights,
                hipStream_t stream);
 
+/*
+ * A plain streaming read, measurement context for the front's roofline (not
+ * a step of the method): how fast the current device streams `bytes` of
+ * device memory with the front's launch shape (256 blocks of 512 threads)
+ * and load shape (non-temporal 16-byte loads, 8 in flight per lane).  Block
+ * b reads the b-th 1/256 of src; thread t of it reads 16-byte pieces t,
+ * t + 512, ... of that share and stores the XOR of their 32-bit words in
+ * sink[512 b + t].
+ *   src   device memory, 16-byte aligned, bytes a whole multiple of 2 MiB
+ *         (256 * 512 * 16), at most 128 GiB (read);
+ *   sink  device memory, unsigned [256 * 512], 4-byte aligned (written).
+ * One launch on `stream`; allocates nothing, never synchronizes.
+ * Errors: QKVF_ERR_NULLPTR, QKVF_ERR_SHAPE (bytes not a positive multiple
+ * of 2 MiB, or too large), QKVF_ERR_ALIGN, QKVF_ERR_DEVICE, QKVF_ERR_HIP.
+ */
+int qkvf_stream_read(const void *src, size_t bytes, unsigned *sink, hipStream_t stream);
+
 /* Synchronize each device that holds a workspace, free every workspace of
  * the library and forget prepared shapes.  No call may be made concurrently
  * from another thread. */

@@ -28,7 +28,8 @@ STATUS = {
 }
 EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
            "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_device_fault", "qkvf_release",
-           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front", "qkvf_route")
+           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front", "qkvf_route",
+           "qkvf_stream_read")
 
 
 class QkvfError(ValueError):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.qkvf_layer_front.restype = I
     L.qkvf_route.argtypes = [P, I64, P, ctypes.c_double, I, P, P, P]
     L.qkvf_route.restype = I
+    L.qkvf_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    L.qkvf_stream_read.restype = I
     L.qkvf_release.argtypes = []
     L.qkvf_release.restype = None
     _lib = L
@@ -216,3 +219,14 @@ def route(logits, bias, route_scale: float, ids, weights, stream=None) -> None:
     st = lib().qkvf_route(_ptr(logits), logits.stride(0), _ptr(bias), float(route_scale),
                           int(logits.shape[0]), _ptr(ids), _ptr(weights), _stream_handle(stream))
     _raise(st, "qkvf_route")
+
+
+STREAM_QUANTUM = 256 * 512 * 16   # qkvf_stream_read reads whole multiples of 2 MiB
+
+
+def stream_read(src, sink, stream=None) -> None:
+    """qkvf_stream_read on torch tensors: src any contiguous device tensor of a
+    whole number of 2 MiB (16-byte aligned), sink int32/uint32 [256 * 512]."""
+    st = lib().qkvf_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                _stream_handle(stream))
+    _raise(st, "qkvf_stream_read")

@@ -12,6 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqkvfront.so")
 SOURCES = [os.path.join(CSRC, "qkvf_api.cpp"), os.path.join(CSRC, "qkvf_kernels.hip"),
            os.path.join(CSRC, "qkvf_attn2.hip"), os.path.join(CSRC, "qkvf_layer_front.hip"),
+           os.path.join(CSRC, "qkvf_stream.hip"),
            os.path.join(CSRC, "qkvf_route.hip")]
 HEADERS = [os.path.join(ROOT, "include", "qkvf.h"), os.path.join(CSRC, "qkvf_internal.h")]
 

@@ -510,3 +510,18 @@ int qkvf_route(const float *logits, int64_t logits_row_stride, const float *bias
                                       ids, weights, stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }
+
+int qkvf_stream_read(const void *src, size_t bytes, unsigned *sink, hipStream_t stream)
+{
+    if (!src || !sink)
+        return QKVF_ERR_NULLPTR;
+    if (bytes == 0 || bytes % kStreamQuantum != 0 || bytes / kStreamQuantum > kStreamMaxQuanta)
+        return QKVF_ERR_SHAPE;
+    if (!aligned(src, 16) || !aligned(sink, 4))
+        return QKVF_ERR_ALIGN;
+    const int ds = checked_device();
+    if (ds != QKVF_OK)
+        return ds;
+    const hipError_t e = launch_stream_read(src, bytes, sink, stream);
+    return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
+}

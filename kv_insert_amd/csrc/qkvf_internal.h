@@ -63,6 +63,13 @@ hipError_t check_placement(unsigned *scratch, bool *round_robin);
 // (0 on error).  The kernel needs all kGrid blocks resident together.
 int blocks_per_cu(int nkv);
 
+// The streaming-read probe: kGrid blocks of kStreamThreads threads; a buffer
+// is a whole number of kStreamQuantum bytes (one 16-byte piece per thread).
+constexpr int kStreamThreads = 512;
+constexpr size_t kStreamQuantum = size_t(kGrid) * kStreamThreads * 16;
+constexpr size_t kStreamMaxQuanta = size_t(1) << 16;   // 128 GiB
+hipError_t launch_stream_read(const void *src, size_t bytes, unsigned *sink, hipStream_t stream);
+
 // attn2: softmax scale is 1/sqrt(64) (applied in the kernel), o-norm epsilon.
 constexpr float kAttn2Eps = 1e-6f;
 // A split's partial of one query row: max, sum, 2 words of padding, O[64].

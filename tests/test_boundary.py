@@ -197,3 +197,14 @@ def test_layer_front_refusals_before_the_device(L):
     assert L.qkvf_layer_front(None, 0, 1, None, 1e-6, P, None, P, None) == 5
     assert L.qkvf_layer_front(P + 16, 1, 1, None, 1e-6, P, None, P, None) == 4
     assert L.qkvf_layer_front(P, 0, 1, P + 2, 1e-6, P, None, P, None) == 4
+
+
+def test_stream_read_refusals_before_the_device(L):
+    P, Q = 1 << 21, qf.STREAM_QUANTUM
+    assert L.qkvf_stream_read(None, Q, P, None) == 5
+    assert L.qkvf_stream_read(P, Q, None, None) == 5
+    assert L.qkvf_stream_read(P, 0, P, None) == 2
+    assert L.qkvf_stream_read(P, Q + 16, P, None) == 2
+    assert L.qkvf_stream_read(P, (1 << 16) * Q + Q, P, None) == 2
+    assert L.qkvf_stream_read(P + 8, Q, P, None) == 4
+    assert L.qkvf_stream_read(P, Q, P + 2, None) == 4
