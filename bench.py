@@ -583,6 +583,16 @@ def main():
                               "frac_of_8TBs": round(ogbs / HBM_PEAK_GBS, 4),
                               "weight_sets_rotated": rotated_sets(o, 0)}),
                   file=sys.stderr, flush=True)
+        # Context per weight size: the plain streaming read of one weight
+        # set, rotated over as many sets as the front's sweep points use.
+        for k in wl.SWEEP_NKV:
+            sw = wl.sweep(1, k)
+            ctx = stream_context(sw, rotated_sets(sw, 0), a.steps, a.repeats)
+            print(json.dumps({"workload": f"stream_read_n{sw.N}", "bytes_per_call": ctx["bytes_per_call"],
+                              "us_per_call": ctx["us_per_call"], "GB_per_s": ctx["GB_per_s"],
+                              "frac_of_8TBs": ctx["frac_of_8TBs"],
+                              "buffers_rotated": ctx["buffers_rotated"]}),
+                  file=sys.stderr, flush=True)
         for aw in wl.ATTN2_WORKLOADS.values():
             if aw is wl.A0:   # the small parity case, not a timing workload
                 continue
