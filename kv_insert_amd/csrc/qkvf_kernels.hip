@@ -57,6 +57,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Buffer descriptor word 3 for raw 32-bit buffer access, and the cache bits
 // of a device-coherent (sc1) buffer load: it is served by the XCD's L2 when
@@ -323,6 +324,21 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         constexpr int kSplitBytes = int(sizeof(uint64_t)) * N;  // times M, below
         // One 16-byte load per split reads the two columns' words; each 8-byte
         // half was stored whole and is checked on its own.
+        // With NKV = 1 a full round reads 32 splits x 16 bytes per lane, so the
+        // wave first polls lightly: lane pi watches one word (its first column
+        // in split pi % S) until every lane's word is this call's; the full
+        // read below still checks every tag.  (Measured faster for NKV = 1
+        // only; with fewer splits the extra round costs more than it saves.)
+        if constexpr (NKV == 1) {
+            for (unsigned tries = 0;; ++tries) {
+                asm volatile("" ::: "memory");
+                const u32x2 w0 = __builtin_amdgcn_raw_buffer_load_b64(
+                    rsrc, base + (pi % Sh::S) * M * kSplitBytes, 0, kCacheSc1);
+                if (__all(w0.y == target) || tries >= kSpinLimit)
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
         u32x4 v[Sh::S];
         for (unsigned tries = 0;; ++tries) {
             // Every round must issue its loads again: keep the compiler from
