@@ -133,18 +133,26 @@ def cpu_baseline(w: wl.Workload, budget_s: float) -> dict | None:
     xb = wl.bits(x)
     table = wl.rope_table(w.table_rows).numpy()
     cache = np.zeros((w.pages, w.nkv, wl.PAGE_SLOTS, wl.SLOT_WIDTH), np.uint16)
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        oracle.front(xb, W, pos.numpy(), slots.numpy(), table, w.nkv, wl.EPS, cache,
-                     nthreads=threads)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or (el / calls) * (calls + 1) > 2 * budget_s:
-            break
-    per_call = el / calls
+    def timed(nthreads: int, budget: float):
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            oracle.front(xb, W, pos.numpy(), slots.numpy(), table, w.nkv, wl.EPS, cache,
+                         nthreads=nthreads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget or (el / calls) * (calls + 1) > 2 * budget:
+                return el / calls, calls
+
+    per_call, calls = timed(threads, budget_s)
+    # The same oracle on one core, for a third of the budget (at least one call).
+    one, one_calls = timed(1, budget_s / 3)
     return {"value": round(w.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
             "us_per_call": round(per_call * 1e6, 1), "cores": threads, "kind": "oracle",
-            "sample": f"{calls} full oracle calls of {w.name} (weight set 0), {threads} OpenMP threads"}
+            "sample": f"{calls} full oracle calls of {w.name} (weight set 0), {threads} OpenMP threads",
+            "single_core": {"value": round(w.algorithmic_bytes() / one / 1e9, 4), "unit": "GB/s",
+                            "us_per_call": round(one * 1e6, 1), "cores": 1,
+                            "sample": f"{one_calls} full oracle calls of {w.name} (weight set 0), "
+                                      "1 thread"}}
 
 
 def stream_context(w: wl.Workload, sets: int, steps: int, repeats: int) -> dict:

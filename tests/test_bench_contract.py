@@ -81,3 +81,15 @@ def test_committed_counter_records_have_their_fields():
             assert name in table
             b = entry.get("hbm_bytes_per_launch", entry.get("hbm_bytes_per_call"))
             assert b > table[name].algorithmic_bytes() * 0.9
+
+
+def test_cpu_baseline_reports_all_cores_and_one_core():
+    """The oracle is timed on the host's cores and on one core, each on full
+    calls of the workload, with the sample stated."""
+    import bench
+    from kv_insert_amd import workloads as wl
+    r = bench.cpu_baseline(wl.C1, 0.5)
+    assert r["kind"] == "oracle" and r["cores"] >= 1 and r["us_per_call"] > 0
+    one = r["single_core"]
+    assert one["cores"] == 1 and one["us_per_call"] > 0 and "1 thread" in one["sample"]
+    assert r["value"] > 0 and one["value"] > 0
