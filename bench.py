@@ -182,7 +182,7 @@ def stream_context(w: wl.Workload, sets: int, steps: int, repeats: int) -> dict:
     del bufs
     torch.cuda.empty_cache()
     return {"kernel": "qkvf_stream_read (plain streaming read, 256 x 512 threads, "
-                      "8 x 16-byte non-temporal loads in flight per lane)",
+                      "16 x 16-byte non-temporal loads in flight per lane)",
             "bytes_per_call": nbytes, "buffers_rotated": sets,
             "us_per_call": round(ms * 1e3, 3), "GB_per_s": round(gbs, 1),
             "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}

@@ -287,7 +287,7 @@ int qkvf_route(const float *logits, int64_t logits_row_stride, const float *bias
  * A plain streaming read, measurement context for the front's roofline (not
  * a step of the method): how fast the current device streams `bytes` of
  * device memory with the front's launch shape (256 blocks of 512 threads)
- * and load shape (non-temporal 16-byte loads, 8 in flight per lane).  Block
+ * and load shape (non-temporal 16-byte loads), 16 in flight per lane.  Block
  * b reads the b-th 1/256 of src; thread t of it reads 16-byte pieces t,
  * t + 512, ... of that share and stores the XOR of their 32-bit words in
  * sink[512 b + t].

@@ -22,7 +22,7 @@ def host_xor(words: np.ndarray, quanta: int) -> np.ndarray:
     return np.bitwise_xor.reduce(np.bitwise_xor.reduce(pieces, axis=3), axis=1).reshape(-1)
 
 
-@pytest.mark.parametrize("quanta", [1, 3, 8, 9, 20])
+@pytest.mark.parametrize("quanta", [1, 3, 8, 9, 16, 17, 20, 32])
 def test_stream_read_reads_every_byte(quanta):
     n = quanta * qf.STREAM_QUANTUM // 4
     g = torch.Generator().manual_seed(500 + quanta)
