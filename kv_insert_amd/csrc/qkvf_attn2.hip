@@ -18,18 +18,19 @@
 // read.  Keys then stream in steps of 128 (one chunk of 32 per key group):
 // each thread loads one 16-byte piece of K and of V of one slot, with
 // kDepth steps of loads in flight (a register ring), and stages them in LDS
-// as K [128 keys][64] (16-byte pieces XOR-swizzled by key) and, per key
-// group, V^T [64][32 keys] (groups of 4 keys XOR-swizzled by dimension).
+// as K [128 keys][64] and V [128 keys][64], both with their 16-byte pieces
+// XOR-swizzled by key (one 16-byte write each).
 // Each key group's waves then take their 32 keys:
 //   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, A = 16 keys, B = 16 query rows;
 //                 lane l holds query l % 16 and keys 4 (l / 16) + v),
 //   weights 2^(scale s - m) against a reference point m that trails the
 //                 running max by at most 16 log2 units (rescaled only in a
 //                 rare wave-uniform branch),
-//   O^T += V^T P^T (A = 16 dims x the lane group's 8 keys, B = the lane's 8
-//                 weights as bf16 hi + lo parts, so no lane exchange is
-//                 needed and the weights keep ~16 bits); the row sums come
-//                 from the same parts through an all-ones A operand.
+//   O^T += V^T P^T (A = 16 dims x the lane group's 8 keys, read from the
+//                 key-major V by the transposing LDS read ds_read_b64_tr_b16;
+//                 B = the lane's 8 weights as bf16 hi + lo parts, so no lane
+//                 exchange is needed and the weights keep ~16 bits); the row
+//                 sums come from the same parts through an all-ones A operand.
 // After the loop the 4 key groups merge in LDS.  With one split the block
 // finishes its rows itself; otherwise it writes (max, sum, O) per row to the
 // workspace and attn2_merge, one wave per output row, combines the splits in
@@ -44,6 +45,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))   // LDS pointers of the builtins
 
 constexpr int kChunk = 32;                     // keys of one MFMA pass (two pages)
 constexpr int kGroups = 4;                     // key groups (chunks) per step
@@ -69,22 +71,11 @@ static_assert(kAttn2MaxSplits <= 64, "the merge gives each split one lane");
 
 __device__ inline float sigmoidf(float g) { return 1.f / (1.f + __expf(-g)); }
 
-// LDS layouts of a staged chunk, chosen so that the 16-byte K writes and
-// reads, the 2-byte V^T writes and the 8-byte V^T reads are free of bank
-// conflicts (checked with the LDS bank-conflict counter).
-//  K [32 keys][64 dims]: 16-byte piece p of key k at piece p ^ (k % 8).
+// LDS layout of a staged step, K and V alike: [128 keys][64 dims], 16-byte
+// piece p of key k at piece p ^ (k % 8), so that the 16-byte writes, the
+// 16-byte K reads and the 8-byte transposing V reads each touch every bank
+// equally often.
 __device__ inline int kswz(int key) { return key & 7; }
-//  V^T [64 dims][32 keys]: row d at row vrow(d); the group of 4 keys
-//  k / 4 at group (k / 4) ^ vgrp(d), with bits d1, d2 ^ d4, d3 ^ d5.
-__device__ inline int vrow(int d) { return d ^ ((d >> 3) & 1); }
-__device__ inline int vgrp(int d)
-{
-    return ((d >> 1) & 1) | ((((d >> 2) ^ (d >> 4)) & 1) << 1) | ((((d >> 3) ^ (d >> 5)) & 1) << 2);
-}
-__device__ inline int vt_index(int d, int key)
-{
-    return vrow(d) * kChunk + ((((key >> 2) ^ vgrp(d)) << 2) | (key & 3));
-}
 
 // How request length L is cut for Z splits: keys from `base` (the page of
 // the earliest attended key) in chunks of 32, `per` chunks per split (whole
@@ -128,7 +119,7 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
             const int32_t *__restrict__ seq_lens, int max_len, int window, int Z,
             float *__restrict__ ws, __bf16 *__restrict__ out, int64_t out_stride)
 {
-    // Two step buffers of K [128 keys][64] and V^T [4 groups][64][32 keys];
+    // Two step buffers of K [128 keys][64] and V [128 keys][64];
     // after the key loop the same bytes hold the groups' O for the merge.
     __shared__ __attribute__((aligned(16))) __bf16 stage_lds[2][2 * kStep * kHeadDim];
     __shared__ int64_t pg[kSegPages];   // element offset of each page's K|V rows
@@ -173,12 +164,20 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
 
     // Step layout: thread tid moves slot kl = tid / 8 of the step's 128 keys,
     // 16-byte part p = tid % 8 of its K (dims 8 p ..) and of its V: K rows of
-    // all 128 keys, then one V^T block per group (layouts above).
+    // all 128 keys, then V rows of all 128 keys (layout above).
     const int kl = tid >> 3, part = tid & 7;
     const int k_lds = kl * kHeadDim + 8 * (part ^ kswz(kl));
-    const int v_lds = kStep * kHeadDim + (kl >> 5) * (kHeadDim * kChunk);
+    const int v_lds = kStep * kHeadDim + kl * kHeadDim + 8 * (part ^ kswz(kl));
     const int kg_lds = kChunk * grp * kHeadDim;                          // group's K rows
-    const int vg_lds = kStep * kHeadDim + grp * (kHeadDim * kChunk);     // group's V^T
+    const int vg_lds = kStep * kHeadDim + grp * (kHeadDim * kChunk);     // group's V rows
+    // The V operand comes from ds_read_b64_tr_b16: every lane supplies the
+    // address of 4 consecutive elements, and within each group of 16 lanes,
+    // lane c receives element c % 4 of the 4 loaded by lanes 4 e + c / 4, as
+    // its element e (e = 0..3).  Lane c of lane group g therefore addresses
+    // key 4 g + c / 4 (and 16 more), dims 16 dt + 4 (c % 4) .. + 3, and gets
+    // dim 16 dt + c of keys 4 g .. 4 g + 3 (and 16 more).
+    const int trk = 4 * g + (c >> 2);
+    const int tr_off = trk * kHeadDim + 4 * (c & 1);
     const __bf16 *kv_head = kv_cache + int64_t(j) * kPageSlots * kSlotWidth + part * 8;
     const int64_t page_elems = int64_t(nkv) * kPageSlots * kSlotWidth;
 
@@ -214,16 +213,14 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
                 vp = ok ? vp : bf16x8{};
             }
             *reinterpret_cast<bf16x8 *>(&stage_lds[sb][k_lds]) = kp;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                stage_lds[sb][v_lds + vt_index(8 * part + e, kl & 31)] = vp[e];
+            *reinterpret_cast<bf16x8 *>(&stage_lds[sb][v_lds]) = vp;
         };
 
         // The group's 32 keys of a step from buffer `buf` (a constant at every
         // call): scores, online softmax, products.
         auto compute = [&](int k0, int buf) {
             const __bf16 *Ks = &stage_lds[buf][kg_lds];
-            const __bf16 *Vt = &stage_lds[buf][vg_lds];
+            const __bf16 *Vg = &stage_lds[buf][vg_lds];
             // S^T for 32 keys: two key tiles of 16 (A row = lane % 16).
             f32x4 s[2];
 #pragma unroll
@@ -302,10 +299,13 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
                 // V^T row 16 dt + c (A row = lane % 16): keys 4 g .. and
-                // 16 + 4 g .. (4 consecutive keys stay together).
-                const int d = 16 * dt + c;
-                const bf16x4 va = *reinterpret_cast<const bf16x4 *>(&Vt[vt_index(d, 4 * g)]);
-                const bf16x4 vb = *reinterpret_cast<const bf16x4 *>(&Vt[vt_index(d, 16 + 4 * g)]);
+                // 16 + 4 g .. (4 consecutive keys stay together).  The 8-byte
+                // half c % 2 of piece 2 dt + (c % 4) / 2, swizzled by key.
+                const int pc = 8 * ((2 * dt + ((c & 3) >> 1)) ^ kswz(trk));
+                const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (LDS_AS bf16x4 *)(&Vg[tr_off + pc]));
+                const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (LDS_AS bf16x4 *)(&Vg[16 * kHeadDim + tr_off + pc]));
                 const bf16x8 vv = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, ph, o[dt], 0, 0, 0);
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pl, o[dt], 0, 0, 0);
