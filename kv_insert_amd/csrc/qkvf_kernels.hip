@@ -62,8 +62,10 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // Buffer descriptor word 3 for raw 32-bit buffer access, and the cache bits
 // of a device-coherent (sc1) buffer load: it is served by the XCD's L2 when
 // the writer ran on the same XCD, and sees other XCDs' write-through stores.
+// kCacheNt marks a load non-temporal.
 constexpr int kBufferConfig = 0x00020000;
 constexpr int kCacheSc1 = 16;
+constexpr int kCacheNt = 2;
 
 constexpr float kEps = 1e-6f;
 
@@ -97,9 +99,12 @@ __device__ inline bf16x8 load16(const __bf16 *p)
 }
 
 // W is read once: non-temporal loads keep it from displacing reused lines.
-__device__ inline bf16x8 stream16(const __bf16 *p)
+// They go through a buffer descriptor over W with 32-bit byte offsets, which
+// measured faster than global loads of 64-bit addresses with the same policy.
+__device__ inline bf16x8 stream16(__amdgpu_buffer_rsrc_t w, int off)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(w, off, 0, kCacheNt);
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ inline unsigned pack2(__bf16 lo, __bf16 hi)
@@ -187,15 +192,20 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
 
     // Load j of this wave covers chunk c of tile row `row` (rows 2w, 2w+1);
     // it lands in LDS chunk row * C + (c ^ row).
-    const __bf16 *wtile = W + size_t(group * U * kTileRows) * kHidden + k0;
-    size_t goff[LD];
+    // Byte offsets into W, which is at most 9216 x 8192 bf16 (151 MB).
+    static_assert(size_t(N) * kHidden * 2 < (size_t(1) << 31), "W offsets fit 31 bits");
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(W), 0, int(size_t(N) * kHidden * 2), kBufferConfig);
+    const int wtile = int((size_t(group * U * kTileRows) * kHidden + k0) * 2);
+    constexpr int kTileBytes = int(kTileStride * 2);
+    int goff[LD];
     int loff[LD];
 #pragma unroll
     for (int j = 0; j < LD; ++j) {
         const int L = j * 64 + lane;
         const int row = 2 * wave + L / C;
         const int c = L % C;
-        goff[j] = size_t(row) * kHidden + c * 8;
+        goff[j] = (row * kHidden + c * 8) * 2;
         loff[j] = (row * C + (c ^ (row & 15))) * 16;
     }
 
@@ -204,7 +214,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     for (int u = 0; u < D; ++u)
 #pragma unroll
         for (int j = 0; j < LD; ++j)
-            ring[u][j] = stream16(wtile + u * kTileStride + goff[j]);
+            ring[u][j] = stream16(wr, wtile + u * kTileBytes + goff[j]);
     if constexpr (NKV != 1)
         load_x();
 
@@ -259,7 +269,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         if (u + D < U) {
 #pragma unroll
             for (int j = 0; j < LD; ++j)
-                ring[u % D][j] = stream16(wtile + (u + D) * kTileStride + goff[j]);
+                ring[u % D][j] = stream16(wr, wtile + (u + D) * kTileBytes + goff[j]);
         }
         __syncthreads();
         if constexpr (kReduceInLoop) {
