@@ -1,12 +1,15 @@
 """bench.py's contract that runs without a GPU: more than one GPU is refused
 with a message before anything touches a device, unknown workloads are
 refused, the workloads' algorithmic byte counts are the documented
-formulas at the documented sizes, and counter traffic is reported only for
-the kernel source it was measured on."""
+formulas at the documented sizes, counter traffic is reported only for
+the kernel source it was measured on, and the committed counter records add
+up."""
 import json
 import os
 import subprocess
 import sys
+
+import pytest
 
 from kv_insert_amd import workloads as wl
 
@@ -81,6 +84,29 @@ def test_committed_counter_records_have_their_fields():
             assert name in table
             b = entry.get("hbm_bytes_per_launch", entry.get("hbm_bytes_per_call"))
             assert b > table[name].algorithmic_bytes() * 0.9
+
+
+def test_committed_counter_records_add_up():
+    """Each record's HBM bytes are its own counter readings (KiB per
+    dispatch) scaled by its copy calibration: FETCH_SIZE x fetch factor +
+    WRITE_SIZE x write factor, summed over the call's kernels."""
+    for path in (bench.COUNTERS, bench.LF_COUNTERS):
+        rec = json.load(open(path))
+        cal = rec["calibration"]
+        assert cal["fetch_factor"] == pytest.approx(
+            cal["copy_bytes_read"] / 1024 / cal["copy_FETCH_SIZE_KiB"], rel=1e-4)
+        assert cal["write_factor"] == pytest.approx(
+            cal["copy_bytes_written"] / 1024 / cal["copy_WRITE_SIZE_KiB"], rel=1e-4)
+        for entry in rec["workloads"].values():
+            b = entry.get("hbm_bytes_per_launch", entry.get("hbm_bytes_per_call"))
+            expect = 1024 * (entry["FETCH_SIZE_KiB"] * cal["fetch_factor"]
+                             + entry["WRITE_SIZE_KiB"] * cal["write_factor"])
+            assert b == pytest.approx(expect, abs=1.0)
+    rec = json.load(open(bench.ATTN2_COUNTERS))
+    for entry in rec["workloads"].values():
+        expect = 1024 * ((entry["split_fetch_kib"] + entry["merge_fetch_kib"]) * rec["fetch_scale"]
+                         + (entry["split_write_kib"] + entry["merge_write_kib"]) * rec["write_scale"])
+        assert entry["hbm_bytes_per_call"] == pytest.approx(expect, abs=1.0)
 
 
 def test_cpu_baseline_reports_all_cores_and_one_core():
