@@ -151,8 +151,8 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
 
     // Q^T operand: lane (c, g) holds q[row][head][32 s + 8 g .. + 7], s = 0, 1.
     const __bf16 *qrow = q + row * q_stride + int64_t(head) * kHeadDim;
-    const bf16x8 qv0 = *reinterpret_cast<const bf16x8 *>(qrow + 8 * g);
-    const bf16x8 qv1 = *reinterpret_cast<const bf16x8 *>(qrow + 32 + 8 * g);
+    const bf16x8 qv0 = *reinterpret_cast<const bf16x8 *>(qrow + attn2_q_piece(g, 0));
+    const bf16x8 qv1 = *reinterpret_cast<const bf16x8 *>(qrow + attn2_q_piece(g, 1));
 
     float m = -INFINITY;   // reference point of this lane's query (log2 units)
     f32x4 o[4] = {};       // O^T[16 dt + 4 g + v][c]
@@ -195,15 +195,18 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
         // Loads are issued unconditionally, so that the number of loads behind
         // each ring slot is the same on every path and the wait before staging
         // a slot leaves the later slots in flight; a step past the segment
-        // (never staged) reads the block's own q row, already in cache.  A key
-        // outside [klo, khi) loads a valid key and is zeroed at staging.
+        // (never staged) reads the two pieces of the block's own q head that
+        // the Q operand holds, already in cache and inside the head's 64
+        // values.  A key outside [klo, khi) loads a valid key and is zeroed at
+        // staging.
         auto issue = [&](int k0, bool real, bf16x8 *ring) {
             const int key = min(max(k0 + kl, klo), khi - 1);
             const __bf16 *src =
                 kv_head + pg[key / kPageSlots - page0] + (key & (kPageSlots - 1)) * kSlotWidth;
-            src = real ? src : qrow + 8 * g;
-            ring[0] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(src));
-            ring[1] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(src + kHeadDim));
+            const __bf16 *src_k = real ? src : qrow + attn2_q_piece(g, 0);
+            const __bf16 *src_v = real ? src + kHeadDim : qrow + attn2_q_piece(g, 1);
+            ring[0] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(src_k));
+            ring[1] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(src_v));
         };
         auto stage = [&](int k0, int sb, const bf16x8 *ring) {
             bf16x8 kp = ring[0], vp = ring[1];

@@ -75,6 +75,13 @@ constexpr float kAttn2Eps = 1e-6f;
 // A split's partial of one query row: max, sum, 2 words of padding, O[64].
 constexpr int kAttn2PartialFloats = 4 + kHeadDim;
 constexpr int kAttn2MaxReqs = 64;
+// The 8-value piece of a 64-value query head that lane group g (0..3) holds
+// in half h (0, 1) of the Q operand: values 32 h + 8 g .. + 7.  A key-loop
+// step past a block's keys loads these pieces instead of a K|V slot, so
+// every read of q stays inside the head's row.
+constexpr int attn2_q_piece(int g, int h) { return 32 * h + 8 * g; }
+static_assert(attn2_q_piece(3, 1) + 8 <= kHeadDim && attn2_q_piece(0, 0) >= 0,
+              "q pieces lie inside the head");
 
 // Key splits of an attn2 launch.  A request's rows span at most
 // max_model_len keys (window + 7 with a window); the keys are cut into about

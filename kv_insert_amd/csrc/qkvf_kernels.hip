@@ -350,6 +350,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             }
         }
         u32x4 v[Sh::S];
+        bool gave_up = false;
         for (unsigned tries = 0;; ++tries) {
             // Every round must issue its loads again: keep the compiler from
             // hoisting them out of the loop.
@@ -367,6 +368,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
                 break;
             if (tries >= kSpinLimit) {
                 words[kFaultWord] = kFaultTimeout;
+                gave_up = true;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -400,10 +402,14 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             o1 = __bf16(n1 * rc + n0 * rs);
         }
         const unsigned packed = pack2(o0, o1);
-        if (tok_ok)
+        // A wave that gave up holds stale sums: it stores nothing, so the
+        // cache never receives them (its y and cache entries keep their old
+        // contents and the fault word says the call failed).
+        const bool store = tok_ok && !gave_up;
+        if (store)
             *reinterpret_cast<unsigned *>(y + size_t(tok) * N + n) = packed;
 
-        if (tok_ok && slot_t >= 0 && h >= NQ && h < NQ + 2 * NKV) {
+        if (store && slot_t >= 0 && h >= NQ && h < NQ + 2 * NKV) {
             const int64_t page = slot_t / kPageSlots, off = slot_t % kPageSlots;
             const bool is_k = h < NQ + NKV;
             const int j = is_k ? h - NQ : h - NQ - NKV;

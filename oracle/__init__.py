@@ -51,9 +51,15 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        build()
-    lib = ctypes.CDLL(LIB)
+    # QKVF_ORACLE_LIB names another build of qkvf_oracle.c (the sanitizer
+    # test loads one compiled with -fsanitize=address,undefined).
+    other = os.environ.get("QKVF_ORACLE_LIB")
+    if other:
+        lib = ctypes.CDLL(other)
+    else:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        lib = ctypes.CDLL(LIB)
     P = ctypes.c_void_p
     lib.qkvfo_float_to_bf16.restype = ctypes.c_uint16
     lib.qkvfo_float_to_bf16.argtypes = [ctypes.c_float]
