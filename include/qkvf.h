@@ -22,9 +22,12 @@
  * identical.
  *
  * All pointers are device pointers on the current HIP device.  The caller
- * owns every tensor; the library owns only a small fp32 workspace per device
- * (allocated by qkvf_prepare, freed by qkvf_release).  Functions return 0 or
- * a qkvf_status code, never throw and never abort.
+ * owns every tensor; the library owns only a small workspace per device
+ * (allocated by qkvf_prepare, freed by qkvf_release) through which the
+ * kernel's blocks pass their fp32 partial sums.  Every call leaves that
+ * workspace as it found it, so no call depends on an earlier one (no
+ * counters, no state across calls).  Functions return 0 or a qkvf_status
+ * code, never throw and never abort.
  */
 #ifndef QKVF_H
 #define QKVF_H
@@ -64,9 +67,9 @@ typedef enum { QKVF_DTYPE_BF16 = 0, QKVF_DTYPE_F32 = 1 } qkvf_dtype;
  * row count 1..M on the current device (qkv_front page, function "prepare":
  * ready the variants before graph capture).  Validates the shape, checks the
  * device is gfx950 with room for the kernel's 256 blocks at once (one per
- * CU), allocates and zeroes the device workspace once (about 4.7 MB, the same
- * for every shape) and checks on which XCD each block runs (both synchronize
- * the device, once), and binds
+ * CU), allocates and sets up the device workspace once (about 2.4 MB, the
+ * same for every shape) and checks on which XCD each block runs (both
+ * synchronize the device, once), and binds
  * (N, num_kv_heads) as the calling thread's
  * current shape, which qkvf_run uses.  Call it again to switch shape; it is
  * cheap after the first call.  Not to be called during graph capture.
@@ -95,17 +98,19 @@ int qkvf_prepare(int N, int num_kv_heads, int M);
  * distinct non-negative slots, and no overlap between y, kv_cache and the
  * inputs (qkvf_check verifies all of these).  The call allocates nothing,
  * never synchronizes and only enqueues work on `stream` (so it can be
- * captured in a HIP graph, and replayed any number of times).  Calls on one
- * device share its workspace and need all 256 CUs: they must be ordered (one
- * stream, or streams ordered by events) and not overlap other calls of this
- * library on the device.  A call that cannot make progress (calls
- * overlapped) gives up after a bounded wait, leaves invalid outputs and
- * records a fault that qkvf_device_fault reports.  Partials pass between
- * blocks tagged with a 32-bit call number: a stale partial could be taken
- * only if its workspace position was last written a whole multiple of 2^32
- * calls earlier (a position unused for 2^32 calls, then used again);
- * qkvf_release followed by qkvf_prepare zeroes the workspace and restarts
- * the count.
+ * captured in a HIP graph, and replayed any number of times).
+ * Ordering: calls on one device share its workspace, so they must not run
+ * concurrently (issue them on one stream, or order streams with events).
+ * Calls that do overlap are undefined: they can take each other's partial
+ * sums and write wrong y and cache entries without any fault being
+ * recorded.  Residency: the kernel's 256 blocks (one per CU) wait for each
+ * other's partials; other work on the device only delays the blocks that
+ * have not started yet.  A block that waits far longer than any call takes
+ * (about a second) gives up: it stores no y and no cache entry and records
+ * a fault in the device's fault word (qkvf_fault_word, qkvf_device_fault).
+ * While the fault word is set, every call on the device stores nothing
+ * (y and kv_cache keep their contents), until qkvf_device_fault reports and
+ * clears it.
  * Errors (cheap scalar checks only): QKVF_ERR_NOT_PREPARED, QKVF_ERR_ROWS,
  * QKVF_ERR_NULLPTR, QKVF_ERR_ALIGN, QKVF_ERR_DEVICE, QKVF_ERR_HIP.
  */
@@ -159,14 +164,34 @@ size_t qkvf_workspace_bytes(void);
 int qkvf_set_handoff(int mode);
 
 /*
+ * For tests of the failure path: the polling rounds a block of a later
+ * qkvf_run waits for another block's partials before it gives up (stores
+ * nothing for its part and records a fault).  rounds == 0 restores the
+ * default (about a second); 1 gives up at the first round that finds a
+ * partial missing.  Process-wide.  Returns QKVF_OK.
+ */
+int qkvf_set_spin_limit(unsigned rounds);
+
+/*
  * Synchronize the current device and report whether any call on it since the
- * last query gave up waiting for a partial result (QKVF_ERR_TIMEOUT; the
- * outputs of that call are not valid).  Clears the record.  Returns QKVF_OK
- * when no call failed (or nothing was prepared on the device),
- * QKVF_ERR_DEVICE when there is no current HIP device, QKVF_ERR_HIP on a
- * runtime error.
+ * last query gave up waiting for a partial result (QKVF_ERR_TIMEOUT; that
+ * call's missing outputs and every later call's outputs were not written).
+ * Clears the fault and sets the workspace up again, so calls work again.
+ * Returns QKVF_OK when no call failed (or nothing was prepared on the
+ * device), QKVF_ERR_DEVICE when there is no current HIP device, QKVF_ERR_HIP
+ * on a runtime error.
  */
 int qkvf_device_fault(void);
+
+/*
+ * The device address of the current device's fault word (unsigned, 4-byte
+ * aligned, owned by the library until qkvf_release): 0 while every call has
+ * completed, nonzero once a call gave up waiting.  A caller can copy it on
+ * its own stream after its calls, without synchronizing the device; only
+ * qkvf_device_fault clears it.  Errors: QKVF_ERR_NULLPTR (word == NULL),
+ * QKVF_ERR_DEVICE, QKVF_ERR_NOT_PREPARED (no workspace on this device).
+ */
+int qkvf_fault_word(unsigned **word);
 
 /*
  * attn2: paged decode attention of the 8-token verify step fused with the

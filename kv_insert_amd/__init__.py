@@ -27,7 +27,9 @@ STATUS = {
     10: "QKVF_ERR_OVERLAP", 11: "QKVF_ERR_MEMORY", 12: "QKVF_ERR_TIMEOUT",
 }
 EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
-           "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_device_fault", "qkvf_release",
+           "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_set_spin_limit",
+           "qkvf_device_fault", "qkvf_fault_word",
+           "qkvf_release",
            "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front", "qkvf_route",
            "qkvf_stream_read")
 
@@ -70,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.qkvf_set_handoff.restype = I
     L.qkvf_device_fault.argtypes = []
     L.qkvf_device_fault.restype = I
+    L.qkvf_set_spin_limit.argtypes = [ctypes.c_uint]
+    L.qkvf_set_spin_limit.restype = I
+    L.qkvf_fault_word.argtypes = [P]
+    L.qkvf_fault_word.restype = I
     L.qkvf_attn2_prepare.argtypes = [I, I, I, I]
     L.qkvf_attn2_prepare.restype = I
     L.qkvf_attn2_run.argtypes = [P, I64, P, I64, P, P, I64, P, I, P, I64, P]
@@ -157,10 +163,24 @@ def set_handoff(mode: int) -> None:
     _raise(lib().qkvf_set_handoff(int(mode)), "qkvf_set_handoff")
 
 
+def set_spin_limit(rounds: int) -> None:
+    """qkvf_set_spin_limit: polling rounds before a block gives up (0 = the
+    default); for tests of the failure path."""
+    _raise(lib().qkvf_set_spin_limit(int(rounds)), "qkvf_set_spin_limit")
+
+
 def device_fault() -> int:
     """qkvf_device_fault: synchronize; 0, or QKVF_ERR_TIMEOUT if a call on the
     current device gave up waiting (its outputs are then invalid)."""
     return int(lib().qkvf_device_fault())
+
+
+def fault_word_address() -> int:
+    """qkvf_fault_word: the device address of the current device's fault
+    word (nonzero once a call gave up waiting)."""
+    p = ctypes.c_void_p()
+    _raise(lib().qkvf_fault_word(ctypes.byref(p)), "qkvf_fault_word")
+    return int(p.value)
 
 
 def release() -> None:

@@ -26,7 +26,7 @@ constexpr int kMaxDevices = 64;
 // fields without it: a workspace is published (release) only once it is
 // initialised, and a row count is marked prepared only after that.
 struct DeviceState {
-    std::atomic<float *> ws{nullptr};
+    std::atomic<unsigned *> ws{nullptr};
     std::atomic<bool> round_robin{false};     // blocks with equal b % 8 verified to share an XCD
     std::atomic<unsigned> prepared[9] = {};   // per nkv: bit m set once rows m are prepared
     // Split partials of attn2.  A larger workspace is published before its
@@ -42,6 +42,7 @@ struct DeviceState {
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 std::atomic<bool> g_force_coherent{false};    // qkvf_set_handoff(1)
+std::atomic<unsigned> g_spin_limit{kSpinLimit};  // qkvf_set_spin_limit
 
 // Shape bound by the last qkvf_prepare of this thread.
 thread_local int t_N = 0;
@@ -139,12 +140,12 @@ int qkvf_prepare(int N, int num_kv_heads, int M)
     }
     if (st.ws.load(std::memory_order_relaxed) == nullptr) {
         void *p = nullptr;
-        if (hipMalloc(&p, kWorkspaceFloats * sizeof(float)) != hipSuccess) {
+        if (hipMalloc(&p, kWorkspaceWords * sizeof(unsigned)) != hipSuccess) {
             (void)hipGetLastError();
             return QKVF_ERR_ALLOC;
         }
-        // Epoch, fault word and ready flags start at zero.
-        if (hipMemset(p, 0, kWorkspaceFloats * sizeof(float)) != hipSuccess ||
+        // Every partial word starts empty and the fault word clear.
+        if (reset_workspace(static_cast<unsigned *>(p), nullptr) != hipSuccess ||
             hipDeviceSynchronize() != hipSuccess) {
             (void)hipGetLastError();
             (void)hipFree(p);
@@ -160,7 +161,7 @@ int qkvf_prepare(int N, int num_kv_heads, int M)
             return QKVF_ERR_HIP;
         }
         st.round_robin.store(rr, std::memory_order_relaxed);
-        st.ws.store(static_cast<float *>(p), std::memory_order_release);
+        st.ws.store(static_cast<unsigned *>(p), std::memory_order_release);
     }
     st.prepared[num_kv_heads].fetch_or((2u << M) - 2u, std::memory_order_release);  // rows 1..M
     t_N = N;
@@ -186,13 +187,14 @@ int qkvf_run(const void *x, const void *W, const int64_t *positions, const int64
     const DeviceState &st = g_dev[dev];
     if (!(st.prepared[t_nkv].load(std::memory_order_acquire) & (1u << M)))
         return QKVF_ERR_NOT_PREPARED;
-    float *ws = st.ws.load(std::memory_order_acquire);
+    unsigned *ws = st.ws.load(std::memory_order_acquire);
     if (ws == nullptr)   // released meanwhile
         return QKVF_ERR_NOT_PREPARED;
     const bool coherent = g_force_coherent.load(std::memory_order_relaxed) ||
                           !st.round_robin.load(std::memory_order_relaxed);
     const hipError_t e = launch_front(t_nkv, M, x, W, positions, slots, cos_sin, y, kv_cache,
-                                      ws, coherent, stream);
+                                      ws, coherent, g_spin_limit.load(std::memory_order_relaxed),
+                                      stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }
 
@@ -275,7 +277,7 @@ const char *qkvf_strerror(int status)
     case QKVF_ERR_RANGE: return "a position or slot is out of range, or a slot repeats";
     case QKVF_ERR_OVERLAP: return "y or kv_cache overlaps another operand";
     case QKVF_ERR_MEMORY: return "a pointer is not device memory of the current device";
-    case QKVF_ERR_TIMEOUT: return "a call on this device gave up waiting for a partial result (calls overlapped, or the device placed blocks on XCDs differently than at prepare) and its output is not valid";
+    case QKVF_ERR_TIMEOUT: return "a call on this device gave up waiting for a partial result (its blocks could not all run, or the device placed blocks on XCDs differently than at prepare); it and every call after it stored nothing until this report";
     default: return "unknown qkvf status";
     }
 }
@@ -297,7 +299,7 @@ int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block, int 
     return QKVF_OK;
 }
 
-size_t qkvf_workspace_bytes(void) { return kWorkspaceFloats * sizeof(float); }
+size_t qkvf_workspace_bytes(void) { return kWorkspaceWords * sizeof(unsigned); }
 
 int qkvf_set_handoff(int mode)
 {
@@ -307,30 +309,51 @@ int qkvf_set_handoff(int mode)
     return QKVF_OK;
 }
 
+int qkvf_set_spin_limit(unsigned rounds)
+{
+    g_spin_limit.store(rounds == 0 ? kSpinLimit : rounds - 1, std::memory_order_relaxed);
+    return QKVF_OK;
+}
+
 int qkvf_device_fault(void)
 {
     std::lock_guard<std::mutex> lock(g_mu);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QKVF_ERR_DEVICE;
-    float *ws = g_dev[dev].ws.load(std::memory_order_acquire);
+    unsigned *ws = g_dev[dev].ws.load(std::memory_order_acquire);
     if (ws == nullptr)
         return QKVF_OK;
     unsigned word = 0;
-    unsigned *fault = reinterpret_cast<unsigned *>(ws) + kFaultWord;
     if (hipDeviceSynchronize() != hipSuccess ||
-        hipMemcpy(&word, fault, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) {
+        hipMemcpy(&word, ws + kFaultWord, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) {
         (void)hipGetLastError();
         return QKVF_ERR_HIP;
     }
     if (word == 0)
         return QKVF_OK;
-    const unsigned zero = 0;
-    if (hipMemcpy(fault, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) {
+    // Leave the fault state: empty every partial word (a call that gave up
+    // may have left some full) and clear the fault word.
+    if (reset_workspace(ws, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipGetLastError();
         return QKVF_ERR_HIP;
     }
     return QKVF_ERR_TIMEOUT;
+}
+
+int qkvf_fault_word(unsigned **word)
+{
+    if (word == nullptr)
+        return QKVF_ERR_NULLPTR;
+    *word = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKVF_ERR_DEVICE;
+    unsigned *ws = g_dev[dev].ws.load(std::memory_order_acquire);
+    if (ws == nullptr)
+        return QKVF_ERR_NOT_PREPARED;
+    *word = ws + kFaultWord;
+    return QKVF_OK;
 }
 
 void qkvf_release(void)
@@ -342,7 +365,7 @@ void qkvf_release(void)
         DeviceState &st = g_dev[d];
         for (auto &bits : st.prepared)   // first, so no launch starts on a freed workspace
             bits.store(0);
-        float *ws = st.ws.exchange(nullptr);
+        unsigned *ws = st.ws.exchange(nullptr);
         float *aws = st.attn2_ws.exchange(nullptr);
         st.attn2_ws_floats.store(0);
         if (ws != nullptr || aws != nullptr || !st.retired.empty()) {

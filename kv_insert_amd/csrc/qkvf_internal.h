@@ -27,32 +27,39 @@ constexpr int cols_for(int nkv) { return 2 * (kQPerKv + 1) * nkv * kHeadDim; }
 // tile-splits for every supported nkv.
 constexpr int splits_for(int nkv) { return 32 / nkv; }
 
-// Workspace layout (32-bit words): tagged partials [splits][M][N] as 64-bit
-// words {fp32 partial, call number} (splits * N = 36864 for every nkv,
-// M <= 16), then a sticky fault word, then one flag per projection block
-// that counts the calls the block has finished, then scratch words for the
-// placement check.
-constexpr size_t kPartialWords = size_t(32) * 1152 * kMaxRows;  // 64-bit words
-constexpr size_t kFaultWord = 2 * kPartialWords;
-constexpr size_t kReadyOffset = kFaultWord + 64;
-constexpr size_t kPlacementOffset = kReadyOffset + kGrid;  // scratch of check_placement
-constexpr size_t kWorkspaceFloats = kPlacementOffset + kGrid;
+// Workspace layout (32-bit words): partials [splits][M][N], one fp32 word
+// each (splits * N = 36864 for every nkv, M <= 16), then a sticky fault word,
+// then scratch words for the placement check.  Between calls every partial
+// word holds kPartialEmpty: each call's readers empty the words they consumed.
+constexpr size_t kPartialWords = size_t(32) * 1152 * kMaxRows;
+constexpr size_t kFaultWord = kPartialWords;
+constexpr size_t kPlacementOffset = kFaultWord + 64;  // scratch of check_placement
+constexpr size_t kWorkspaceWords = kPlacementOffset + kGrid;
+// An empty partial word: a NaN bit pattern.  A partial whose fp32 sum has
+// exactly these bits (a NaN from NaN inputs) is stored as kPartialNan.
+constexpr unsigned kPartialEmpty = 0xFFFFFFFFu;
+constexpr unsigned kPartialNan = 0x7FC00000u;
 
 // Iterations (each with a short sleep) a wave waits for a partial before it
-// gives up and records a fault; far longer than any call takes.
+// gives up and records a fault; far longer than any call takes (about a
+// second).  qkvf_set_spin_limit lowers it for tests of the failure path.
 constexpr unsigned kSpinLimit = 1u << 20;
 
 // Fault word values.
 constexpr unsigned kFaultTimeout = 1;    // a wait gave up
 
 // Enqueue one front call on `stream`.  Shapes were validated by the caller;
-// ws holds kWorkspaceFloats words on this device, zeroed before first use.
+// ws holds kWorkspaceWords words on this device, set up by reset_workspace.
 // coherent: every partial is stored write-through (the safe mode when the
 // blocks with equal b % 8 are not known to share an XCD).
 hipError_t launch_front(int nkv, int M, const void *x, const void *W,
                         const int64_t *positions, const int64_t *slots,
                         const float *cos_sin, void *y, void *kv_cache,
-                        float *ws, bool coherent, hipStream_t stream);
+                        unsigned *ws, bool coherent, unsigned spin_limit, hipStream_t stream);
+
+// Enqueue a kernel on `stream` that empties every partial word of ws and
+// clears its fault word (no hipMemset, so it may be captured).
+hipError_t reset_workspace(unsigned *ws, hipStream_t stream);
 
 // Launch a kGrid-block kernel on the current device, one block per CU, and
 // report whether blocks were placed on XCDs round robin (block b on XCD

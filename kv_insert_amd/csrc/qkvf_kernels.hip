@@ -17,30 +17,35 @@
 //        the block's K range, and issues v_mfma_f32_16x16x32_bf16 with W as
 //        the 16-row A operand and the tokens (x, held in registers for the
 //        whole kernel, zero past M) as the 16 B columns.
-//    The 8 wave partials of each tile are summed in LDS in wave order, one
-//    tile behind the stream, and the block's fp32 partial goes to the
-//    workspace, each value stored together with the number of the call in
-//    one 64-bit word.
+//    The 8 wave partials of each tile are summed in LDS in wave order, and
+//    the block's fp32 partials go to the workspace, one 32-bit word each.
 //
 //  Epilogue: each (head, pair of tokens) is one item of one wave, on the XCD
 //    whose blocks produced that head's partials.  The wave fetched its
 //    tokens' slots and cos|sin rows while the weights streamed; it reads the
-//    S partials of each of its columns until all carry this call's number (a
-//    bounded wait, normally served by the XCD's own L2), sums them in
-//    split order, rounds to bf16 (round to nearest even), applies to q and k
-//    heads the weightless RMS norm (sum of squares by a butterfly of lane
-//    exchanges) and the interleaved rotation, and stores its part of y and of
-//    the token's K|V slot.
+//    S partials of each of its columns until none is empty (a bounded wait,
+//    normally served by the XCD's own L2), sums them in split order, marks
+//    them empty again, rounds to bf16 (round to nearest even), applies to q
+//    and k heads the weightless RMS norm (sum of squares by a butterfly of
+//    lane exchanges) and the interleaved rotation, and stores its part of y
+//    and of the token's K|V slot.
 //
-//  No read-modify-write atomics, no flags to wait for and no cache
-//  maintenance: each partial travels with its call number in one 64-bit
-//  word, stored plainly into the XCD's L2 when its reader runs on the same
-//  XCD and written through (device-coherent, agent scope) otherwise; a
-//  reader's device-coherent loads accept a value only when its tag is the
-//  current call's.  The call number comes from a
-//  per-block counter that every call raises by one (so all counters agree at
-//  the start of a call, and a graph replay gets a new number).  The sums run
-//  in a fixed order, so the result depends on the launch shape only.
+//  No read-modify-write atomics, no flags, no counters and no cache
+//  maintenance.  Between calls every partial word holds kPartialEmpty (a NaN
+//  pattern no partial takes: a partial with those bits is stored as the
+//  canonical NaN), so a word that is not empty holds this call's partial:
+//  each word has one producer and one reader per call, and the reader
+//  empties it after use, so every call leaves the workspace as it found it.
+//  A partial read on the producing XCD is stored plainly into that XCD's L2;
+//  one read on another XCD is written through (device-coherent, agent
+//  scope).  The sums run in a fixed order, so the result depends on the
+//  launch shape only.
+//
+//  A wave that waits too long sets the workspace's fault word and stores
+//  nothing; from then on every call finds the fault word set and runs no
+//  reader, so it stores no y and no cache entry (the workspace may hold
+//  stray partials), until the host clears the fault and empties the
+//  workspace again.
 //
 // Definitions followed: qkv_front page, module summary (projection, norm,
 // RoPE, y store, K/V insert) and "Structure" (partials summed in a fixed
@@ -118,7 +123,8 @@ __global__ void __launch_bounds__(kWaves * 64, 1)
 front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const int64_t *__restrict__ positions, const int64_t *__restrict__ slots,
             const float *__restrict__ cos_sin, __bf16 *__restrict__ y,
-            __bf16 *__restrict__ kv_cache, float *__restrict__ ws, int M, int coherent)
+            __bf16 *__restrict__ kv_cache, unsigned *__restrict__ ws, int M, int coherent,
+            unsigned spin_limit)
 {
     using Sh = Shape<NKV>;
     constexpr int ST = Sh::STEPS, D = Sh::DEPTH, U = kTilesPerBlock, C = Sh::CHUNKS;
@@ -126,16 +132,8 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     constexpr size_t kTileStride = size_t(kTileRows) * kHidden;
     __shared__ __attribute__((aligned(16))) unsigned char lds[Sh::LDS_BYTES];
 
-    unsigned *words = reinterpret_cast<unsigned *>(ws);
-    unsigned *ready = words + kReadyOffset;
-    uint64_t *parts = reinterpret_cast<uint64_t *>(ws);
+    unsigned *parts = ws;
     const int b = blockIdx.x;
-    // Every call raises every block's flag by one, so at the start of a call
-    // all flags hold the number of calls made so far; this call's value is
-    // one more.  A block reads only its own flag, written by itself in the
-    // previous call.
-    const unsigned target =
-        __hip_atomic_load(ready + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
     // Blocks are dispatched to the 8 XCDs round robin: block b runs on XCD
     // (b + c) % 8 for a c that varies between launches.  So the 32 blocks
     // with b % 8 == x share one XCD; they take the S splits of row groups
@@ -218,34 +216,41 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     if constexpr (NKV != 1)
         load_x();
 
-    // The token's rotation for this lane's pair, fetched while W streams.
-    // The barriers keep this dependent load behind the weight prologue, so
-    // waiting for the position never stalls the stream.
+    // The token's rotation for this lane's pair and the fault word, fetched
+    // while W streams.  The barriers keep these loads behind the weight
+    // prologue, so waiting for them never stalls the stream; both are first
+    // needed after the stream.
     __builtin_amdgcn_sched_barrier(0);
     const float *cs_row = cos_sin != nullptr ? cos_sin + pos_t * kHeadDim
                                              : reinterpret_cast<const float *>(ws);
     float rc = cs_row[pi], rs = cs_row[32 + pi];
+    const unsigned fault_in =
+        __hip_atomic_load(ws + kFaultWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_sched_barrier(0);
 
-    // Store the block's partial of (tile u, token t, row): the sum of the 8
-    // waves' partials slab[w][t][row] in wave order (slab: [8][16][17]).
-    auto store_partial = [&](const float *slab, int u, int t, int row) {
+    // The block's partial of (tile u, token t, row): the sum of the 8 waves'
+    // partials slab[w][t][row] in wave order (slab: [8][16][17]).
+    auto block_sum = [&](const float *slab, int t, int row) {
         float sum = slab[t * (kTileRows + 1) + row];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
             sum += slab[(w * kTileRows + t) * (kTileRows + 1) + row];
+        return sum;
+    };
+    auto store_partial = [&](float sum, int u, int t, int row) {
+        unsigned bits = __float_as_uint(sum);
+        bits = bits == kPartialEmpty ? kPartialNan : bits;
         const int n = (group * U + u) * kTileRows + row;
-        const uint64_t word = (uint64_t(target) << 32) | __float_as_uint(sum);
-        uint64_t *dst = parts + (size_t(split) * M + t) * N + n;
+        unsigned *dst = parts + (size_t(split) * M + t) * N + n;
         // The reader of row n runs on the XCD holding its head's first row.
         // On this XCD a plain store is enough (the reader's device-coherent
         // load is served by the shared L2); for another XCD the store writes
         // through to memory.
         const int reader_xcd = (n / kHeadDim) * kHeadDim / XCD_ROWS;
         if (!coherent && reader_xcd == xcd)
-            *dst = word;
+            *dst = bits;
         else
-            __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     constexpr int SLAB = kWaves * kTileRows * (kTileRows + 1);  // floats per tile
 
@@ -253,13 +258,16 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // spare bandwidth: the 8 wave partials of tile u go to red[u & 1] right
     // after its MFMAs and, one barrier later (all waves have written them),
     // are summed and stored while tile u + 1 streams; red[u & 1] is written
-    // again only after the barrier that follows the sum.  Small tiles keep
-    // the loop short and reduce all tiles after it.  Lane (r, q) holds
-    // D[row = 4q + v][token = r], v = 0..3; token columns r >= M are never
-    // needed.
+    // again only after the barrier that follows the sum.  (Keeping the sums
+    // in registers and storing all 9 after the stream measured slower: 25.3
+    // against 24.9 us at M = 8, 26.8 against 26.1 us at M = 16.)  Small
+    // tiles keep the loop short and reduce all tiles after it.  Lane (r, q)
+    // holds D[row = 4q + v][token = r], v = 0..3; token columns r >= M are
+    // never needed.
     constexpr bool kReduceInLoop = NKV >= 4;
     __shared__ float red[kReduceInLoop ? 2 : 1][kReduceInLoop ? SLAB : 1];
     f32x4 acc[kReduceInLoop ? 1 : U];
+    const bool summer = threadIdx.x < kTileRows * M;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         unsigned char *tile = lds + (u & 1) * Sh::TILE_BYTES;
@@ -273,8 +281,9 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         }
         __syncthreads();
         if constexpr (kReduceInLoop) {
-            if (u > 0 && threadIdx.x < kTileRows * M)
-                store_partial(red[(u - 1) & 1], u - 1, threadIdx.x >> 4, threadIdx.x & 15);
+            if (u > 0 && summer)
+                store_partial(block_sum(red[(u - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
+                              u - 1, threadIdx.x >> 4, threadIdx.x & 15);
         }
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -295,8 +304,9 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     }
     if constexpr (kReduceInLoop) {
         __syncthreads();
-        if (threadIdx.x < kTileRows * M)
-            store_partial(red[(U - 1) & 1], U - 1, threadIdx.x >> 4, threadIdx.x & 15);
+        if (summer)
+            store_partial(block_sum(red[(U - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
+                          U - 1, threadIdx.x >> 4, threadIdx.x & 15);
     } else {
         // All tiles at once, in the tile buffers the loop no longer needs.
         float *all = reinterpret_cast<float *>(lds);
@@ -314,42 +324,42 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         for (int e = threadIdx.x; e < U * per_tile; e += kWaves * 64) {
             const int u = e / per_tile;
             const int rem = e - u * per_tile;
-            store_partial(all + u * SLAB, u, rem >> 4, rem & 15);
+            store_partial(block_sum(all + u * SLAB, rem >> 4, rem & 15), u, rem >> 4, rem & 15);
         }
     }
 
-    // Count this call in the block's flag (read back at the next call's start).
-    if (threadIdx.x == 0)
-        __hip_atomic_store(ready + b, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // A device left in the fault state by an earlier call: no reader runs,
+    // so no y or cache entry is stored (partials stored above are emptied
+    // when the host clears the fault).
+    if (fault_in != 0)
+        return;
 
     if (has_item) {
-        // The S partials of this lane's two columns, each tagged with the call
-        // that wrote it: poll (bounded) with device-coherent loads until every
-        // tag is this call's, then sum in split order.  A stale word never
-        // carries this call's tag.
+        // The S partials of this lane's two columns: poll (bounded) with
+        // device-coherent loads until none is empty, then sum in split order
+        // and empty them for the next call.
         const int n = head * kHeadDim + 2 * pi;
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            parts, 0, int(sizeof(uint64_t) * kPartialWords), kBufferConfig);
-        const int base = (tok_c * N + n) * int(sizeof(uint64_t));
-        constexpr int kSplitBytes = int(sizeof(uint64_t)) * N;  // times M, below
-        // One 16-byte load per split reads the two columns' words; each 8-byte
-        // half was stored whole and is checked on its own.
-        // With NKV = 1 a full round reads 32 splits x 16 bytes per lane, so the
+            parts, 0, int(sizeof(unsigned) * kPartialWords), kBufferConfig);
+        const int base = (tok_c * N + n) * int(sizeof(unsigned));
+        const int split_bytes = M * N * int(sizeof(unsigned));
+        // One 8-byte load per split reads the two columns' words; each word
+        // was stored whole and is checked on its own.
+        // With NKV = 1 a full round reads 32 splits x 8 bytes per lane, so the
         // wave first polls lightly: lane pi watches one word (its first column
-        // in split pi % S) until every lane's word is this call's; the full
-        // read below still checks every tag.  (Measured faster for NKV = 1
-        // only; with fewer splits the extra round costs more than it saves.)
+        // in split pi % S) until every lane's word is full; the full read
+        // below still checks every word.  (Measured faster for NKV = 1 only.)
         if constexpr (NKV == 1) {
             for (unsigned tries = 0;; ++tries) {
                 asm volatile("" ::: "memory");
-                const u32x2 w0 = __builtin_amdgcn_raw_buffer_load_b64(
-                    rsrc, base + (pi % Sh::S) * M * kSplitBytes, 0, kCacheSc1);
-                if (__all(w0.y == target) || tries >= kSpinLimit)
+                const unsigned w0 = __builtin_amdgcn_raw_buffer_load_b32(
+                    rsrc, base + (pi % Sh::S) * split_bytes, 0, kCacheSc1);
+                if (__all(w0 != kPartialEmpty) || tries >= spin_limit)
                     break;
                 __builtin_amdgcn_s_sleep(1);
             }
         }
-        u32x4 v[Sh::S];
+        u32x2 v[Sh::S];
         bool gave_up = false;
         for (unsigned tries = 0;; ++tries) {
             // Every round must issue its loads again: keep the compiler from
@@ -357,17 +367,17 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int sp = 0; sp < Sh::S; ++sp)
-                v[sp] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, base + sp * M * kSplitBytes, 0,
-                                                              kCacheSc1);
-            // All loads are in flight before any tag is looked at.
-            unsigned bad = 0;
+                v[sp] = __builtin_amdgcn_raw_buffer_load_b64(rsrc, base + sp * split_bytes, 0,
+                                                             kCacheSc1);
+            // All loads are in flight before any word is looked at.
+            bool empty = false;
 #pragma unroll
             for (int sp = 0; sp < Sh::S; ++sp)
-                bad |= (v[sp].y ^ target) | (v[sp].w ^ target);
-            if (__all(bad == 0))
+                empty |= (v[sp].x == kPartialEmpty) | (v[sp].y == kPartialEmpty);
+            if (__all(!empty))
                 break;
-            if (tries >= kSpinLimit) {
-                words[kFaultWord] = kFaultTimeout;
+            if (tries >= spin_limit) {
+                ws[kFaultWord] = kFaultTimeout;
                 gave_up = true;
                 break;
             }
@@ -377,7 +387,17 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
 #pragma unroll
         for (int sp = 0; sp < Sh::S; ++sp) {
             a0 += __uint_as_float(v[sp].x);
-            a1 += __uint_as_float(v[sp].z);
+            a1 += __uint_as_float(v[sp].y);
+        }
+        // Empty the words for the next call (the lanes of a token past M read
+        // token M - 1's words too, and leave them to that token's lanes).  A
+        // wave that gave up leaves them: the fault state stops later calls.
+        asm volatile("" ::: "memory");
+        if (tok_ok && !gave_up) {
+            unsigned char *pb = reinterpret_cast<unsigned char *>(parts) + base;
+#pragma unroll
+            for (int sp = 0; sp < Sh::S; ++sp)
+                *reinterpret_cast<u32x2 *>(pb + sp * split_bytes) = u32x2{kPartialEmpty, kPartialEmpty};
         }
         const __bf16 p0 = __bf16(a0), p1 = __bf16(a1);
         const float f0 = float(p0), f1 = float(p1);
@@ -418,19 +438,28 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             *reinterpret_cast<unsigned *>(dst) = packed;
         }
     }
-
 }
 
 template <int NKV>
 hipError_t launch(int M, const void *x, const void *W, const int64_t *positions,
                   const int64_t *slots, const float *cos_sin, void *y, void *kv_cache,
-                  float *ws, bool coherent, hipStream_t stream)
+                  unsigned *ws, bool coherent, unsigned spin_limit, hipStream_t stream)
 {
     hipLaunchKernelGGL(front_fused<NKV>, dim3(kGrid), dim3(kWaves * 64), 0, stream,
                        static_cast<const __bf16 *>(x), static_cast<const __bf16 *>(W),
                        positions, slots, cos_sin, static_cast<__bf16 *>(y),
-                       static_cast<__bf16 *>(kv_cache), ws, M, coherent ? 1 : 0);
+                       static_cast<__bf16 *>(kv_cache), ws, M, coherent ? 1 : 0, spin_limit);
     return hipGetLastError();
+}
+
+// Empties the partial words and clears the fault word.
+__global__ void __launch_bounds__(256) reset_words(unsigned *ws)
+{
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < kPartialWords; i += stride)
+        ws[i] = kPartialEmpty;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        ws[kFaultWord] = 0;
 }
 
 // One block per CU, like the front kernel; each records the XCD it runs on.
@@ -461,16 +490,22 @@ int occupancy()
 
 hipError_t launch_front(int nkv, int M, const void *x, const void *W,
                         const int64_t *positions, const int64_t *slots,
-                        const float *cos_sin, void *y, void *kv_cache, float *ws,
-                        bool coherent, hipStream_t stream)
+                        const float *cos_sin, void *y, void *kv_cache, unsigned *ws,
+                        bool coherent, unsigned spin_limit, hipStream_t stream)
 {
     switch (nkv) {
-    case 1: return launch<1>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
-    case 2: return launch<2>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
-    case 4: return launch<4>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
-    case 8: return launch<8>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, stream);
+    case 1: return launch<1>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, spin_limit, stream);
+    case 2: return launch<2>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, spin_limit, stream);
+    case 4: return launch<4>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, spin_limit, stream);
+    case 8: return launch<8>(M, x, W, positions, slots, cos_sin, y, kv_cache, ws, coherent, spin_limit, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t reset_workspace(unsigned *ws, hipStream_t stream)
+{
+    hipLaunchKernelGGL(reset_words, dim3(kGrid), dim3(256), 0, stream, ws);
+    return hipGetLastError();
 }
 
 hipError_t check_placement(unsigned *scratch, bool *round_robin)

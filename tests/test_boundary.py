@@ -74,10 +74,26 @@ def test_plan_rejects_bad_shapes(L):
 
 
 def test_workspace_size_is_constant(L):
-    # 64-bit tagged partials [splits][16 rows][N] with splits * N = 36864 for
-    # every nkv, then 64 words (fault word, padding), 256 call counters and
-    # 256 scratch words
-    assert qf.workspace_bytes() == 36864 * 16 * 8 + 64 * 4 + 256 * 4 + 256 * 4
+    # 32-bit partials [splits][16 rows][N] with splits * N = 36864 for every
+    # nkv, then 64 words (fault word, padding) and 256 scratch words
+    assert qf.workspace_bytes() == 36864 * 16 * 4 + 64 * 4 + 256 * 4
+
+
+def test_fault_word_and_spin_limit_without_a_workspace(L):
+    assert L.qkvf_fault_word(None) == 5
+    word = ctypes.c_void_p(1)
+    res = []
+
+    def fresh():
+        res.append(L.qkvf_fault_word(ctypes.byref(word)))
+
+    t = threading.Thread(target=fresh)
+    t.start()
+    t.join()
+    assert res[0] in (1, 6)          # no device here, or nothing prepared on it
+    assert word.value is None        # cleared on refusal
+    assert L.qkvf_set_spin_limit(1) == 0
+    assert L.qkvf_set_spin_limit(0) == 0
 
 
 @pytest.mark.parametrize("N,nkv,M,code", [
