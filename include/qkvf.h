@@ -119,6 +119,30 @@ int qkvf_run(const void *x, const void *W, const int64_t *positions,
              void *kv_cache, int M, hipStream_t stream);
 
 /*
+ * qkvf_run for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call and kernel, with N and num_kv_heads given per call, no qkvf_prepare,
+ * and the partials passed through the library's static device array instead
+ * of a prepared workspace.  The array holds the partials of any call the
+ * front accepts (M <= 16, N <= 9216: 2.36 MB per device, kept until the
+ * process ends); a larger call is refused (QKVF_ERR_SHAPE, QKVF_ERR_ROWS).
+ * It calls no allocating routine.  The first call on a device sets the
+ * array up (empties it and checks on which XCD each block runs) and
+ * synchronizes the device, so make it before any capture; later calls only
+ * enqueue one launch on `stream`.  Every call on a device shares that
+ * device's array: calls that overlap on one device race (undefined, as for
+ * qkvf_run), so order them on one stream or with events.  Faults behave as
+ * for qkvf_run; qkvf_device_fault reports and clears them.  Pointers,
+ * layouts and the caller's guarantees are those of qkvf_run.
+ * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS, QKVF_ERR_NULLPTR, QKVF_ERR_ALIGN,
+ * QKVF_ERR_DEVICE, QKVF_ERR_HIP.
+ */
+int qkvf_run_static(int N, int num_kv_heads, const void *x, const void *W,
+                    const int64_t *positions, const int64_t *slots,
+                    const float *cos_sin, void *y, void *kv_cache, int M,
+                    hipStream_t stream);
+
+/*
  * Full check of a call before it is launched (qkv_front page, function
  * "unsupported"; cute_ops page, supports_call): shape, rows, alignment,
  * that every pointer is device memory of the current device, that y and

@@ -26,7 +26,7 @@ STATUS = {
     7: "QKVF_ERR_ALLOC", 8: "QKVF_ERR_HIP", 9: "QKVF_ERR_RANGE",
     10: "QKVF_ERR_OVERLAP", 11: "QKVF_ERR_MEMORY", 12: "QKVF_ERR_TIMEOUT",
 }
-EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_check", "qkvf_strerror", "qkvf_plan",
+EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_run_static", "qkvf_check", "qkvf_strerror", "qkvf_plan",
            "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_set_spin_limit",
            "qkvf_device_fault", "qkvf_fault_word",
            "qkvf_release",
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.qkvf_prepare.restype = I
     L.qkvf_run.argtypes = [P, P, P, P, P, P, P, I, P]
     L.qkvf_run.restype = I
+    L.qkvf_run_static.argtypes = [I, I, P, P, P, P, P, P, P, I, P]
+    L.qkvf_run_static.restype = I
     L.qkvf_check.argtypes = [I, I, I, I64, I64, P, P, P, P, P, P, P, I]
     L.qkvf_check.restype = I
     L.qkvf_strerror.argtypes = [I]
@@ -131,6 +133,17 @@ def run(x, W, positions, slots, cos_sin, y, kv_cache, M: int | None = None, stre
     st = lib().qkvf_run(_ptr(x), _ptr(W), _ptr(positions), _ptr(slots), _ptr(cos_sin),
                         _ptr(y), _ptr(kv_cache), M, _stream_handle(stream))
     _raise(st, "qkvf_run")
+
+
+def run_static(x, W, positions, slots, cos_sin, y, kv_cache, num_kv_heads: int,
+               M: int | None = None, stream=None) -> None:
+    """qkvf_run_static: qkvf_run without qkvf_prepare and without any
+    allocation (the partials pass through the library's static array)."""
+    M = x.shape[0] if M is None else int(M)
+    st = lib().qkvf_run_static(int(W.shape[0]), int(num_kv_heads), _ptr(x), _ptr(W),
+                               _ptr(positions), _ptr(slots), _ptr(cos_sin), _ptr(y),
+                               _ptr(kv_cache), M, _stream_handle(stream))
+    _raise(st, "qkvf_run_static")
 
 
 def check(x, W, positions, slots, cos_sin, y, kv_cache, num_kv_heads: int,

@@ -37,6 +37,7 @@ struct DeviceState {
     std::atomic<size_t> attn2_ws_floats{0};
     std::vector<float *> retired;
     int arch_ok = -1;                         // -1 unknown, 0 not gfx950, 1 gfx950
+    unsigned static_ok = 0;                   // per nkv: qkvf_run_static's residency checked
 };
 
 std::mutex g_mu;
@@ -198,6 +199,49 @@ int qkvf_run(const void *x, const void *W, const int64_t *positions, const int64
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }
 
+int qkvf_run_static(int N, int num_kv_heads, const void *x, const void *W,
+                    const int64_t *positions, const int64_t *slots, const float *cos_sin,
+                    void *y, void *kv_cache, int M, hipStream_t stream)
+{
+    const int s = shape_status(N, num_kv_heads, M);
+    if (s != QKVF_OK)
+        return s;
+    if (!x || !W || !positions || !slots || !y || !kv_cache)
+        return QKVF_ERR_NULLPTR;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16) || !aligned(kv_cache, 16) ||
+        !aligned(cos_sin, 16) || !aligned(positions, 8) || !aligned(slots, 8))
+        return QKVF_ERR_ALIGN;
+    int dev = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        const int ds = current_device(&dev);
+        if (ds != QKVF_OK)
+            return ds;
+        DeviceState &st = g_dev[dev];
+        if (!(st.static_ok & (1u << num_kv_heads))) {
+            int cus = 0;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                    hipSuccess ||
+                blocks_per_cu(num_kv_heads) * cus < kGrid) {
+                (void)hipGetLastError();
+                return QKVF_ERR_DEVICE;
+            }
+            st.static_ok |= 1u << num_kv_heads;
+        }
+    }
+    unsigned *ws = nullptr;
+    bool rr = false;
+    if (static_workspace(dev, &ws, &rr) != hipSuccess) {
+        (void)hipGetLastError();
+        return QKVF_ERR_HIP;
+    }
+    const bool coherent = g_force_coherent.load(std::memory_order_relaxed) || !rr;
+    const hipError_t e = launch_front(num_kv_heads, M, x, W, positions, slots, cos_sin, y,
+                                      kv_cache, ws, coherent,
+                                      g_spin_limit.load(std::memory_order_relaxed), stream);
+    return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
+}
+
 int qkvf_check(int N, int num_kv_heads, int M, int64_t pages, int64_t table_rows,
                const void *x, const void *W, const int64_t *positions, const int64_t *slots,
                const float *cos_sin, const void *y, const void *kv_cache, int read_indices)
@@ -321,24 +365,35 @@ int qkvf_device_fault(void)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QKVF_ERR_DEVICE;
-    unsigned *ws = g_dev[dev].ws.load(std::memory_order_acquire);
-    if (ws == nullptr)
+    // The prepared workspace and qkvf_run_static's, each if present.
+    unsigned *spaces[2] = {g_dev[dev].ws.load(std::memory_order_acquire),
+                           static_workspace_if_set(dev)};
+    if (spaces[0] == nullptr && spaces[1] == nullptr)
         return QKVF_OK;
-    unsigned word = 0;
-    if (hipDeviceSynchronize() != hipSuccess ||
-        hipMemcpy(&word, ws + kFaultWord, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) {
+    if (hipDeviceSynchronize() != hipSuccess) {
         (void)hipGetLastError();
         return QKVF_ERR_HIP;
     }
-    if (word == 0)
-        return QKVF_OK;
-    // Leave the fault state: empty every partial word (a call that gave up
-    // may have left some full) and clear the fault word.
-    if (reset_workspace(ws, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        (void)hipGetLastError();
-        return QKVF_ERR_HIP;
+    int status = QKVF_OK;
+    for (unsigned *ws : spaces) {
+        if (ws == nullptr)
+            continue;
+        unsigned word = 0;
+        if (hipMemcpy(&word, ws + kFaultWord, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) {
+            (void)hipGetLastError();
+            return QKVF_ERR_HIP;
+        }
+        if (word == 0)
+            continue;
+        // Leave the fault state: empty every partial word (a call that gave
+        // up may have left some full) and clear the fault word.
+        if (reset_workspace(ws, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+            (void)hipGetLastError();
+            return QKVF_ERR_HIP;
+        }
+        status = QKVF_ERR_TIMEOUT;
     }
-    return QKVF_ERR_TIMEOUT;
+    return status;
 }
 
 int qkvf_fault_word(unsigned **word)

@@ -61,6 +61,13 @@ hipError_t launch_front(int nkv, int M, const void *x, const void *W,
 // clears its fault word (no hipMemset, so it may be captured).
 hipError_t reset_workspace(unsigned *ws, hipStream_t stream);
 
+// The library's static workspace on device `dev` (current): set up at the
+// first call on the device (its address, emptied, placement checked; this
+// synchronizes the device), then returned at once.  Allocates nothing.
+hipError_t static_workspace(int dev, unsigned **ptr, bool *round_robin);
+// The static workspace of `dev` if it has been set up, else nullptr.
+unsigned *static_workspace_if_set(int dev);
+
 // Launch a kGrid-block kernel on the current device, one block per CU, and
 // report whether blocks were placed on XCDs round robin (block b on XCD
 // (b + c) % 8 for some c).  scratch holds kGrid words.  Synchronous.

@@ -54,6 +54,9 @@
 // blocks) and the attn2 contract (cache layout).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "qkvf_internal.h"
 
 namespace qkvf {
@@ -506,6 +509,59 @@ hipError_t reset_workspace(unsigned *ws, hipStream_t stream)
 {
     hipLaunchKernelGGL(reset_words, dim3(kGrid), dim3(256), 0, stream, ws);
     return hipGetLastError();
+}
+
+// The workspace of qkvf_run_static: one array per device, of the same
+// layout as a prepared workspace (partials of any shape the front accepts,
+// the fault word and the placement scratch: kWorkspaceWords words, 2.36 MB).
+// Host code uses only its device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned scratch[kWorkspaceWords];
+
+namespace {
+constexpr int kStaticDevices = 64;
+std::mutex g_static_mu;
+std::atomic<unsigned *> g_static_ptr[kStaticDevices] = {};
+std::atomic<bool> g_static_rr[kStaticDevices] = {};
+}  // namespace
+
+hipError_t static_workspace(int dev, unsigned **ptr, bool *round_robin)
+{
+    if (dev < 0 || dev >= kStaticDevices)
+        return hipErrorInvalidDevice;
+    unsigned *p = g_static_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        p = g_static_ptr[dev].load(std::memory_order_acquire);
+        if (p == nullptr) {
+            // Once per device, with that device current: its copy of the
+            // array, emptied, and where the kernel's blocks run on it.
+            void *addr = nullptr;
+            hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            unsigned *q = static_cast<unsigned *>(addr);
+            e = reset_workspace(q, nullptr);
+            if (e == hipSuccess)
+                e = hipDeviceSynchronize();
+            bool rr = false;
+            if (e == hipSuccess)
+                e = check_placement(q + kPlacementOffset, &rr);
+            if (e != hipSuccess)
+                return e;
+            g_static_rr[dev].store(rr, std::memory_order_relaxed);
+            g_static_ptr[dev].store(q, std::memory_order_release);
+            p = q;
+        }
+    }
+    *ptr = p;
+    *round_robin = g_static_rr[dev].load(std::memory_order_relaxed);
+    return hipSuccess;
+}
+
+unsigned *static_workspace_if_set(int dev)
+{
+    return dev >= 0 && dev < kStaticDevices ? g_static_ptr[dev].load(std::memory_order_acquire)
+                                            : nullptr;
 }
 
 hipError_t check_placement(unsigned *scratch, bool *round_robin)

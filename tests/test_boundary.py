@@ -224,3 +224,17 @@ def test_stream_read_refusals_before_the_device(L):
     assert L.qkvf_stream_read(P, (1 << 16) * Q + Q, P, None) == 2
     assert L.qkvf_stream_read(P + 8, Q, P, None) == 4
     assert L.qkvf_stream_read(P, Q, P + 2, None) == 4
+
+
+def test_run_static_refusals_before_the_device(L):
+    P = 1 << 20
+    args = [P, P, P, P, P, P, P]
+    assert L.qkvf_run_static(1152, 3, *args, 1, None) == 2
+    assert L.qkvf_run_static(1000, 1, *args, 1, None) == 2
+    assert L.qkvf_run_static(1152, 1, *args, 0, None) == 3
+    assert L.qkvf_run_static(1152, 1, *args, 17, None) == 3
+    assert L.qkvf_run_static(1152, 1, None, P, P, P, P, P, P, 1, None) == 5
+    assert L.qkvf_run_static(1152, 1, P + 8, P, P, P, P, P, P, 1, None) == 4
+    import torch
+    if not torch.cuda.is_available():
+        assert L.qkvf_run_static(1152, 1, *args, 1, None) == 1
