@@ -10,7 +10,7 @@ namespace qkvf {
 int g_stub_launches = 0;
 
 hipError_t launch_front(int, int, const void *, const void *, const int64_t *, const int64_t *,
-                        const float *, void *, void *, float *, bool, hipStream_t)
+                        const float *, void *, void *, unsigned *, bool, unsigned, hipStream_t)
 {
     ++g_stub_launches;
     return hipErrorInvalidValue;
@@ -51,5 +51,23 @@ hipError_t launch_route(const float *, int64_t, const float *, double, int, int3
     ++g_stub_launches;
     return hipErrorInvalidValue;
 }
+
+}  // namespace qkvf
+
+namespace qkvf {
+
+hipError_t reset_workspace(unsigned *, hipStream_t)
+{
+    ++g_stub_launches;
+    return hipErrorInvalidValue;
+}
+
+hipError_t static_workspace(int, unsigned **, bool *)
+{
+    ++g_stub_launches;
+    return hipErrorInvalidValue;
+}
+
+unsigned *static_workspace_if_set(int) { return nullptr; }
 
 }  // namespace qkvf
