@@ -85,6 +85,17 @@ def parse():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MB",
                     help="instead of the front, time device-to-device copies of MB megabytes "
                          "(a plain copy kernel of known size, for scaling memory counters)")
+    ap.add_argument("--all-cpu-seconds", type=float, default=2.0,
+                    help="CPU time budget of the oracle baseline of each --all line (0 = skip)")
+    ap.add_argument("--profile-workloads", default="", metavar="W1,W2,...",
+                    help="instead of timing, issue warmup + steps front calls of each workload "
+                         "in turn on one stream (for a rocprofv3 run); one JSON line per "
+                         "workload on stdout names its calls, in order")
+    ap.add_argument("--summarize-profiles", default="", metavar="DIR",
+                    help="no GPU: read the rocprofv3 output of a --profile-workloads run under "
+                         "DIR (order.jsonl, trace/, fetch/, write/, calib_fetch/, calib_write/, "
+                         "optionally all.jsonl from --all), write the per-workload counter "
+                         "record to profiles/front_fused_counters.json and print a table")
     return ap.parse_args()
 
 
@@ -119,7 +130,17 @@ class Pool:
                self.cache, M=self.w.M, stream=stream)
 
 
-def cpu_baseline(w: wl.Workload, budget_s: float) -> dict | None:
+def host_threads() -> tuple[int, int]:
+    """(threads the oracle uses, cores this process may run on).  All the
+    cores the process may run on, unless OMP_NUM_THREADS sets the machine's
+    share for one GPU lower."""
+    host = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    limit = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(host, int(limit)) if limit.isdigit() and int(limit) > 0 else host
+    return max(1, threads), host
+
+
+def cpu_baseline(w: wl.Workload, budget_s: float, single_core: bool = True) -> dict | None:
     """The oracle, as it stands, on full calls of the same workload (set 0),
     timed on this host's cores; as many calls as fit the budget (>= 1)."""
     if budget_s <= 0:
@@ -127,7 +148,7 @@ def cpu_baseline(w: wl.Workload, budget_s: float) -> dict | None:
     import numpy as np
 
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, host = host_threads()
     x, pos, slots = wl.make_tokens(w, 0)
     W = wl.bits(wl.make_weights(w, 0))
     xb = wl.bits(x)
@@ -144,15 +165,19 @@ def cpu_baseline(w: wl.Workload, budget_s: float) -> dict | None:
                 return el / calls, calls
 
     per_call, calls = timed(threads, budget_s)
-    # The same oracle on one core, for a third of the budget (at least one call).
-    one, one_calls = timed(1, budget_s / 3)
-    return {"value": round(w.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
-            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "kind": "oracle",
-            "sample": f"{calls} full oracle calls of {w.name} (weight set 0), {threads} OpenMP threads",
-            "single_core": {"value": round(w.algorithmic_bytes() / one / 1e9, 4), "unit": "GB/s",
-                            "us_per_call": round(one * 1e6, 1), "cores": 1,
-                            "sample": f"{one_calls} full oracle calls of {w.name} (weight set 0), "
-                                      "1 thread"}}
+    out = {"value": round(w.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
+           "us_per_call": round(per_call * 1e6, 1), "cores": threads, "host_cores": host,
+           "kind": "oracle",
+           "sample": f"{calls} full oracle calls of {w.name} (weight set 0), {threads} OpenMP "
+                     f"threads on a host whose process may run on {host} cores"}
+    if single_core:
+        # The same oracle on one core, for a third of the budget (>= 1 call).
+        one, one_calls = timed(1, budget_s / 3)
+        out["single_core"] = {"value": round(w.algorithmic_bytes() / one / 1e9, 4), "unit": "GB/s",
+                              "us_per_call": round(one * 1e6, 1), "cores": 1,
+                              "sample": f"{one_calls} full oracle calls of {w.name} (weight set 0), "
+                                        "1 thread"}
+    return out
 
 
 def stream_context(w: wl.Workload, sets: int, steps: int, repeats: int) -> dict:
@@ -279,8 +304,7 @@ def attn2_cpu_baseline(a: wl.Attn2Workload, budget_s: float) -> dict | None:
     if budget_s <= 0:
         return None
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    threads, host = host_threads()   # the OpenMP default team: OMP_NUM_THREADS, else every core
     a1 = dataclasses.replace(a, sets=1)
     y = wl.make_attn2_y(a1, 0)
     q, g = wl.attn2_views(y, a.nkv)
@@ -297,9 +321,10 @@ def attn2_cpu_baseline(a: wl.Attn2Workload, budget_s: float) -> dict | None:
             break
     per_call = el / calls
     return {"value": round(a.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
-            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "kind": "oracle",
+            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "host_cores": host,
+            "kind": "oracle",
             "sample": f"{calls} full oracle calls of {a.name} (request set 0), "
-                      f"OpenMP over (row, head) pairs, up to {threads} threads"}
+                      f"OpenMP over (row, head) pairs, {threads} threads"}
 
 
 def attn2_line(a: wl.Attn2Workload, args) -> dict:
@@ -423,7 +448,7 @@ def layer_front_cpu_baseline(w: wl.LayerFrontWorkload, budget_s: float) -> dict 
     if budget_s <= 0:
         return None
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, host = host_threads()   # the OpenMP default team: OMP_NUM_THREADS, else every core
     x = wl.make_lf_x(w, 0)
     xn = x.numpy() if w.fp32_input else wl.bits(x)
     weight = wl.make_lf_weight(w)
@@ -437,8 +462,10 @@ def layer_front_cpu_baseline(w: wl.LayerFrontWorkload, budget_s: float) -> dict 
             break
     per_call = el / calls
     return {"value": round(w.algorithmic_bytes() / per_call / 1e9, 4), "unit": "GB/s",
-            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "kind": "oracle",
-            "sample": f"{calls} full oracle calls of {w.name} (input set 0), OpenMP over rows"}
+            "us_per_call": round(per_call * 1e6, 1), "cores": threads, "host_cores": host,
+            "kind": "oracle",
+            "sample": f"{calls} full oracle calls of {w.name} (input set 0), OpenMP over rows, "
+                      f"{threads} threads"}
 
 
 def layer_front_line(w: wl.LayerFrontWorkload, args) -> dict:
@@ -540,8 +567,204 @@ def copy_calibration(mb: float, steps: int) -> None:
                       "ms_per_copy": round(ms, 6)}), flush=True)
 
 
+def profile_workloads(names: list[str], steps: int, warmup: int) -> None:
+    """warmup + steps eager calls per workload, announced before they are
+    issued, for a profiler to attribute its per-dispatch records."""
+    for name in names:
+        w = workload_by_name(name)
+        sets = rotated_sets(w, 0)
+        pool = Pool(w, sets)
+        qf.prepare(w.N, w.nkv, w.M)
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_workload": w.name, "M": w.M, "num_kv_heads": w.nkv, "N": w.N,
+                          "front_dispatches": warmup + steps, "warmup": warmup,
+                          "weight_sets_rotated": sets,
+                          "algorithmic_bytes": w.algorithmic_bytes()}), flush=True)
+        with torch.cuda.stream(stream):
+            for i in range(warmup + steps):
+                pool.call(i, stream)
+        torch.cuda.synchronize()
+        del pool
+        torch.cuda.empty_cache()
+    fault = qf.device_fault()
+    if fault != 0:
+        raise RuntimeError(f"a profiled call gave up waiting: {qf.strerror(fault)}")
+
+
+def _csv_rows(directory: str, suffix: str) -> list[dict]:
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _front_rows(rows: list[dict], counter: str | None = None) -> list[dict]:
+    out = [r for r in rows if "front_fused" in r["Kernel_Name"]
+           and (counter is None or r.get("Counter_Name") == counter)]
+    return sorted(out, key=lambda r: int(r["Dispatch_Id"]))
+
+
+def _nkv_of(kernel_name: str) -> int:
+    import re
+    m = re.search(r"front_fusedILi(\d+)E", kernel_name) or re.search(r"front_fused<(\d+)>", kernel_name)
+    return int(m.group(1)) if m else -1
+
+
+def _split(rows: list[dict], order: list[dict]) -> dict:
+    """Per workload, its post-warmup rows (dispatches come in the order the
+    workloads were run, each workload's count announced beforehand)."""
+    need = sum(o["front_dispatches"] for o in order)
+    if len(rows) != need:
+        raise SystemExit(f"{len(rows)} front dispatches recorded, {need} announced")
+    out, i = {}, 0
+    for o in order:
+        part = rows[i:i + o["front_dispatches"]]
+        i += o["front_dispatches"]
+        bad = {_nkv_of(r["Kernel_Name"]) for r in part} - {o["num_kv_heads"]}
+        if bad:
+            raise SystemExit(f"{o['profile_workload']}: dispatches of front_fused<{bad}>")
+        out[o["profile_workload"]] = part[o["warmup"]:]
+    return out
+
+
+def summarize_profiles(d: str, out: str | None = None) -> str:
+    import statistics
+    order = [json.loads(l) for l in open(os.path.join(d, "order.jsonl"))
+             if l.startswith("{") and "profile_workload" in l]
+    trace = _split(_front_rows(_csv_rows(os.path.join(d, "trace"), "kernel_trace.csv")), order)
+    fetch = _split(_front_rows(_csv_rows(os.path.join(d, "fetch"), "counter_collection.csv"),
+                               "FETCH_SIZE"), order)
+    write = _split(_front_rows(_csv_rows(os.path.join(d, "write"), "counter_collection.csv"),
+                               "WRITE_SIZE"), order)
+
+    def copy_median(sub: str, counter: str) -> float:
+        rows = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(d, sub),
+                                                               "counter_collection.csv")
+                if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        return statistics.median(rows)
+
+    calib = json.load(open(os.path.join(d, "calibration.json")))
+    copy_fetch, copy_write = copy_median("calib_fetch", "FETCH_SIZE"), copy_median("calib_write",
+                                                                                 "WRITE_SIZE")
+    fetch_factor = calib["copy_bytes_read"] / (copy_fetch * 1024)
+    write_factor = calib["copy_bytes_written"] / (copy_write * 1024)
+    events = {}
+    all_path = os.path.join(d, "all.jsonl")
+    if os.path.exists(all_path):
+        for l in open(all_path):
+            if l.startswith("{") and '"workload"' in l:
+                rec = json.loads(l)
+                events[rec["workload"]] = rec
+    record = {"kernel": "front_fused<nkv>", "kernel_sha256_16": kernel_hash(),
+              "calibration": {"copy_bytes_read": calib["copy_bytes_read"],
+                              "copy_bytes_written": calib["copy_bytes_written"],
+                              "copy_FETCH_SIZE_KiB": copy_fetch, "copy_WRITE_SIZE_KiB": copy_write,
+                              "fetch_factor": round(fetch_factor, 5),
+                              "write_factor": round(write_factor, 5)},
+              "workloads": {}}
+    lines = ["| Workload | M | KV heads | N | bench.py us/call | trace avg us (min / max) | "
+             "algorithmic GB/s | frac of 8 TB/s | FETCH KiB | WRITE KiB | HBM bytes (scaled) | "
+             "traffic / algorithmic | counter GB/s | oracle us/call (threads / host cores) |",
+             "|" + "---|" * 14]
+    for o in order:
+        name = o["profile_workload"]
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace[name]]
+        f_kib = statistics.median(float(r["Counter_Value"]) for r in fetch[name])
+        w_kib = statistics.median(float(r["Counter_Value"]) for r in write[name])
+        hbm = f_kib * 1024 * fetch_factor + w_kib * 1024 * write_factor
+        alg = o["algorithmic_bytes"]
+        avg = sum(dur) / len(dur)
+        record["workloads"][name] = {
+            "FETCH_SIZE_KiB": f_kib, "WRITE_SIZE_KiB": w_kib,
+            "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes_per_launch": alg,
+            "trace_avg_us": round(avg, 3), "trace_min_us": round(min(dur), 3),
+            "trace_max_us": round(max(dur), 3), "trace_dispatches": len(dur),
+            "counter_dispatches": len(fetch[name])}
+        ev = events.get(name, {})
+        us = ev.get("us_per_call")
+        base = ev.get("cpu_baseline") or {}
+        gbs = alg / (us * 1e-6) / 1e9 if us else None
+        cell = lambda v, f: "n/a" if v is None else f.format(v)
+        lines.append(
+            f"| {name} | {o['M']} | {o['num_kv_heads']} | {o['N']} | {cell(us, '{:.2f}')} | "
+            f"{avg:.2f} ({min(dur):.2f} / {max(dur):.2f}) | {cell(gbs, '{:.0f}')} | "
+            f"{cell(gbs and gbs / HBM_PEAK_GBS, '{:.3f}')} | {f_kib:.1f} | {w_kib:.1f} | "
+            f"{hbm:,.0f} | {hbm / alg:.3f} | {hbm / (avg * 1e-6) / 1e9:.0f} | "
+            f"{cell(base.get('us_per_call'), '{:,.0f}')} ({base.get('cores', '-')} / "
+            f"{base.get('host_cores', '-')}) |")
+    out = out or os.path.join(ROOT, "profiles", "front_fused_counters.json")
+    with open(out, "w") as fh:
+        json.dump(record, fh, indent=1)
+        fh.write("\n")
+    table = "\n".join(lines)
+    print(table)
+    print(f"\nwrote {out}", file=sys.stderr)
+    return table
+
+
+def all_lines(a) -> None:
+    """One JSON line per workload and sweep point on stderr: timing, the
+    roofline with counter traffic when recorded for this kernel source, and
+    the oracle on this host; then the plain streaming read per weight size,
+    attn2 and LayerFront."""
+    others = list(wl.WORKLOADS.values()) + [wl.sweep(m, k) for k in wl.SWEEP_NKV
+                                            for m in wl.SWEEP_M]
+    for o in others:
+        oms, _ = time_front(o, rotated_sets(o, 0), a.steps, a.warmup, a.repeats)
+        ogbs = o.algorithmic_bytes() / (oms * 1e-3) / 1e9
+        traffic = measured_traffic(o)
+        print(json.dumps({"workload": o.name, "M": o.M, "num_kv_heads": o.nkv, "N": o.N,
+                          "us_per_call": round(oms * 1e3, 3), "GB_per_s": round(ogbs, 1),
+                          "frac_of_8TBs": round(ogbs / HBM_PEAK_GBS, 4),
+                          "weight_sets_rotated": rotated_sets(o, 0),
+                          "roofline": {"bound": "hbm", "kernel": f"front_fused<{o.nkv}>",
+                                       "achieved": round(ogbs, 2), "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": round(ogbs / HBM_PEAK_GBS, 4),
+                                       "traffic": None if traffic is None else int(traffic)},
+                          "cpu_baseline": cpu_baseline(o, a.all_cpu_seconds, single_core=False)}),
+              file=sys.stderr, flush=True)
+    # Context per weight size: the plain streaming read of one weight set,
+    # rotated over as many sets as the front's sweep points use.
+    for k in wl.SWEEP_NKV:
+        sw = wl.sweep(1, k)
+        ctx = stream_context(sw, rotated_sets(sw, 0), a.steps, a.repeats)
+        print(json.dumps({"workload": f"stream_read_n{sw.N}", "bytes_per_call": ctx["bytes_per_call"],
+                          "us_per_call": ctx["us_per_call"], "GB_per_s": ctx["GB_per_s"],
+                          "frac_of_8TBs": ctx["frac_of_8TBs"],
+                          "buffers_rotated": ctx["buffers_rotated"]}),
+              file=sys.stderr, flush=True)
+    for aw in wl.ATTN2_WORKLOADS.values():
+        if aw is wl.A0:   # the small parity case, not a timing workload
+            continue
+        line = attn2_line(aw, a)
+        line["cpu_baseline"] = attn2_cpu_baseline(aw, a.all_cpu_seconds)
+        print(json.dumps({"workload": aw.name, "splits": line["config"]["splits"],
+                          "us_per_call": line["us_per_call"], "GB_per_s": line["value"],
+                          "frac_of_8TBs": line["roofline"]["frac"], "roofline": line["roofline"],
+                          "cpu_baseline": line["cpu_baseline"],
+                          "request_sets_rotated": line["config"]["request_sets_rotated"]}),
+              file=sys.stderr, flush=True)
+    for lw in wl.LAYER_FRONT_WORKLOADS.values():
+        line = layer_front_line(lw, a)
+        line["cpu_baseline"] = layer_front_cpu_baseline(lw, a.all_cpu_seconds)
+        print(json.dumps({"workload": lw.name, "us_per_call": line["us_per_call"],
+                          "GB_per_s": line["value"], "frac_of_8TBs": line["roofline"]["frac"],
+                          "roofline": line["roofline"], "cpu_baseline": line["cpu_baseline"],
+                          "sets_rotated": line["config"]["sets_rotated"]}),
+              file=sys.stderr, flush=True)
+
+
 def main():
     a = parse()
+    if a.summarize_profiles:
+        summarize_profiles(a.summarize_profiles)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU (asked for {a.gpus}); the front is a "
               "single-GPU kernel: several GPUs would each run it on their own KV heads' share "
@@ -553,6 +776,9 @@ def main():
     torch.cuda.set_device(0)
     if a.copy_calibration > 0:
         copy_calibration(a.copy_calibration, a.steps)
+        return
+    if a.profile_workloads:
+        profile_workloads(a.profile_workloads.split(","), a.steps, a.warmup)
         return
     if a.route:
         if a.route not in wl.ROUTE_WORKLOADS:
@@ -581,41 +807,7 @@ def main():
     nbytes = w.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     if a.all:
-        others = list(wl.WORKLOADS.values()) + [wl.sweep(m, k) for k in wl.SWEEP_NKV
-                                                for m in wl.SWEEP_M]
-        for o in others:
-            oms, _ = time_front(o, rotated_sets(o, 0), a.steps, a.warmup, a.repeats)
-            ogbs = o.algorithmic_bytes() / (oms * 1e-3) / 1e9
-            print(json.dumps({"workload": o.name, "M": o.M, "num_kv_heads": o.nkv, "N": o.N,
-                              "us_per_call": round(oms * 1e3, 3), "GB_per_s": round(ogbs, 1),
-                              "frac_of_8TBs": round(ogbs / HBM_PEAK_GBS, 4),
-                              "weight_sets_rotated": rotated_sets(o, 0)}),
-                  file=sys.stderr, flush=True)
-        # Context per weight size: the plain streaming read of one weight
-        # set, rotated over as many sets as the front's sweep points use.
-        for k in wl.SWEEP_NKV:
-            sw = wl.sweep(1, k)
-            ctx = stream_context(sw, rotated_sets(sw, 0), a.steps, a.repeats)
-            print(json.dumps({"workload": f"stream_read_n{sw.N}", "bytes_per_call": ctx["bytes_per_call"],
-                              "us_per_call": ctx["us_per_call"], "GB_per_s": ctx["GB_per_s"],
-                              "frac_of_8TBs": ctx["frac_of_8TBs"],
-                              "buffers_rotated": ctx["buffers_rotated"]}),
-                  file=sys.stderr, flush=True)
-        for aw in wl.ATTN2_WORKLOADS.values():
-            if aw is wl.A0:   # the small parity case, not a timing workload
-                continue
-            line = attn2_line(aw, a)
-            print(json.dumps({"workload": aw.name, "splits": line["config"]["splits"],
-                              "us_per_call": line["us_per_call"], "GB_per_s": line["value"],
-                              "frac_of_8TBs": line["roofline"]["frac"],
-                              "request_sets_rotated": line["config"]["request_sets_rotated"]}),
-                  file=sys.stderr, flush=True)
-        for lw in wl.LAYER_FRONT_WORKLOADS.values():
-            line = layer_front_line(lw, a)
-            print(json.dumps({"workload": lw.name, "us_per_call": line["us_per_call"],
-                              "GB_per_s": line["value"], "frac_of_8TBs": line["roofline"]["frac"],
-                              "sets_rotated": line["config"]["sets_rotated"]}),
-                  file=sys.stderr, flush=True)
+        all_lines(a)
     base = cpu_baseline(w, a.cpu_baseline_seconds)
     traffic = measured_traffic(w)
     context = stream_context(w, sets, a.steps, a.repeats)

@@ -81,7 +81,7 @@ def test_committed_counter_records_have_their_fields():
         assert len(rec["kernel_sha256_16"]) == 16
         assert rec["workloads"]
         for name, entry in rec["workloads"].items():
-            assert name in table
+            assert name in table or (table is wl.WORKLOADS and name.startswith("sweep_m"))
             b = entry.get("hbm_bytes_per_launch", entry.get("hbm_bytes_per_call"))
             assert b > table[name].algorithmic_bytes() * 0.9
 
@@ -109,13 +109,82 @@ def test_committed_counter_records_add_up():
         assert entry["hbm_bytes_per_call"] == pytest.approx(expect, abs=1.0)
 
 
-def test_cpu_baseline_reports_all_cores_and_one_core():
+def test_cpu_baseline_reports_all_cores_and_one_core(monkeypatch):
     """The oracle is timed on the host's cores and on one core, each on full
-    calls of the workload, with the sample stated."""
-    import bench
-    from kv_insert_amd import workloads as wl
+    calls of the workload, with the sample stated: every core the process may
+    run on, unless OMP_NUM_THREADS sets a smaller share."""
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
     r = bench.cpu_baseline(wl.C1, 0.5)
-    assert r["kind"] == "oracle" and r["cores"] >= 1 and r["us_per_call"] > 0
+    host = len(os.sched_getaffinity(0))
+    assert r["kind"] == "oracle" and r["cores"] == host and r["host_cores"] == host
+    assert r["us_per_call"] > 0 and f"{host} cores" in r["sample"]
     one = r["single_core"]
     assert one["cores"] == 1 and one["us_per_call"] > 0 and "1 thread" in one["sample"]
     assert r["value"] > 0 and one["value"] > 0
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    assert bench.host_threads() == (min(2, host), host)
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_profile_summary_splits_dispatches_by_workload(tmp_path):
+    """The summary attributes a profiled run's dispatches to workloads in
+    the announced order, drops each workload's warmup, takes medians of the
+    counters and scales them by the copy calibration."""
+    d = tmp_path
+    order = [{"profile_workload": "m8_nkv8_n9216", "M": 8, "num_kv_heads": 8, "N": 9216,
+              "front_dispatches": 4, "warmup": 1, "algorithmic_bytes": 151_292_032},
+             {"profile_workload": "m1_nkv1_n1152", "M": 1, "num_kv_heads": 1, "N": 1152,
+              "front_dispatches": 3, "warmup": 1, "algorithmic_bytes": 18_893_584}]
+    (d / "order.jsonl").write_text("noise\n" + "\n".join(json.dumps(o) for o in order) + "\n")
+    k8 = "_ZN4qkvf12_GLOBAL__N_111front_fusedILi8EEEvPKDF16b"
+    k1 = "_ZN4qkvf12_GLOBAL__N_111front_fusedILi1EEEvPKDF16b"
+    names = [k8] * 4 + [k1] * 3
+    dur = [99.0, 25.0, 26.0, 27.0, 50.0, 8.0, 9.0]          # us; first of each is warmup
+    trace = [["KERNEL_DISPATCH", 7 + i, names[i], 1000, 1000 + int(dur[i] * 1000)]
+             for i in range(7)]
+    trace.insert(2, ["KERNEL_DISPATCH", 8, "other_kernel", 0, 10])   # not the front
+    trace[3][1] = 9
+    for i, row in enumerate(trace):
+        row[1] = i + 1
+    _write_csv(str(d / "trace" / "run_kernel_trace.csv"),
+               ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], trace)
+    fetch_kib = [1.0, 75000.0, 75010.0, 75020.0, 2.0, 9300.0, 9310.0]
+    write_kib = [1.0, 1200.0, 1201.0, 1202.0, 2.0, 40.0, 41.0]
+    for sub, cname, vals in (("fetch", "FETCH_SIZE", fetch_kib), ("write", "WRITE_SIZE", write_kib)):
+        _write_csv(str(d / sub / "run_counter_collection.csv"),
+                   ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"],
+                   [[i + 1, names[i], cname, vals[i]] for i in range(7)])
+    for sub, cname, v in (("calib_fetch", "FETCH_SIZE", 125000.0),
+                          ("calib_write", "WRITE_SIZE", 250000.0)):
+        _write_csv(str(d / sub / "run_counter_collection.csv"),
+                   ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"],
+                   [[1, "__amd_rocclr_copyBuffer", cname, v], [2, "__amd_rocclr_copyBuffer", cname, v]])
+    (d / "calibration.json").write_text(json.dumps({"copy_bytes_read": 256_000_000,
+                                                    "copy_bytes_written": 256_000_000}))
+    (d / "all.jsonl").write_text(json.dumps({"workload": "m8_nkv8_n9216", "us_per_call": 25.5,
+                                             "cpu_baseline": {"us_per_call": 1e5, "cores": 16,
+                                                              "host_cores": 128}}) + "\n")
+    out = tmp_path / "rec.json"
+    table = bench.summarize_profiles(str(d), str(out))
+    rec = json.load(open(out))
+    e8, e1 = rec["workloads"]["m8_nkv8_n9216"], rec["workloads"]["m1_nkv1_n1152"]
+    assert e8["trace_avg_us"] == pytest.approx(26.0) and e8["trace_dispatches"] == 3
+    assert e1["trace_avg_us"] == pytest.approx(8.5) and e1["trace_min_us"] == pytest.approx(8.0)
+    assert e8["FETCH_SIZE_KiB"] == 75010.0 and e1["WRITE_SIZE_KiB"] == 40.5
+    ff = 256_000_000 / (125000.0 * 1024)
+    assert e8["hbm_bytes_per_launch"] == round(1024 * (75010.0 * ff + 1201.0 * 256_000_000 /
+                                                       (250000.0 * 1024)))
+    assert "| m8_nkv8_n9216 | 8 | 8 | 9216 | 25.50 |" in table and "(16 / 128)" in table
+    # a count that does not match the announcement is refused
+    order[1]["front_dispatches"] = 4
+    (d / "order.jsonl").write_text("\n".join(json.dumps(o) for o in order) + "\n")
+    with pytest.raises(SystemExit):
+        bench.summarize_profiles(str(d), str(out))
