@@ -164,7 +164,9 @@ const char *qkvf_strerror(int status);
 
 /*
  * The launch shape of (N, M): grid blocks of the projection kernel, the
- * split of K across blocks, waves per block and 16-row tiles per block.
+ * split of K across blocks, waves per block and the most 16-row tiles a block
+ * owns (each XCD owns whole heads, heads x * H / 8 .. (x + 1) * H / 8 - 1 of
+ * the H = N / 64, and its 32 blocks share their tiles equally).
  * A pure function of its arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or
  * QKVF_ERR_ROWS.  Any output pointer may be NULL.
  */

@@ -19,13 +19,17 @@ constexpr int kMaxRows = 16;        // tokens per call
 constexpr int kTileRows = 16;       // W rows per MFMA tile
 constexpr int kWaves = 8;           // waves per projection block
 constexpr int kGrid = 256;          // projection blocks: one per CU
-constexpr int kTilesPerBlock = 9;   // 16-row tiles each projection block owns
 
 // Columns for nkv KV heads: [q | k | v | gate] = 2 * (8 + 1) * nkv heads.
 constexpr int cols_for(int nkv) { return 2 * (kQPerKv + 1) * nkv * kHeadDim; }
-// K split across blocks: 72*nkv row tiles * (32/nkv) splits = 2304 = 256 * 9
-// tile-splits for every supported nkv.
-constexpr int splits_for(int nkv) { return 32 / nkv; }
+// K split across blocks: each XCD owns whole heads (18 nkv / 8 of them, 2 or
+// 3 for nkv = 1, 4 or 5 for nkv = 2), and its 32 blocks take the splits of
+// 32 / splits row groups of those heads' 16-row tiles.
+constexpr int splits_for(int nkv) { return nkv == 8 ? 4 : 8; }
+// Heads of XCD x: [x heads / 8, (x + 1) heads / 8), heads = 18 nkv.
+constexpr int xcd_heads(int nkv, int x) { return (x + 1) * 18 * nkv / 8 - x * 18 * nkv / 8; }
+// 16-row tiles of a block on XCD x: 4 per head times splits, over its 32 blocks.
+constexpr int tiles_for(int nkv, int x) { return xcd_heads(nkv, x) * 4 * splits_for(nkv) / (kGrid / 8); }
 
 // Workspace layout (32-bit words): partials [splits][M][N], one fp32 word
 // each (splits * N = 36864 for every nkv, M <= 16), then a sticky fault word,

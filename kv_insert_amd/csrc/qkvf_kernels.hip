@@ -6,8 +6,11 @@
 // does the whole call:
 //
 //  Projection: 256 blocks (one per CU, all resident together) of 8 waves.
-//    Block b owns a contiguous K range of 8192/S (S = 32/nkv splits) and 9
-//    row tiles of 16 W rows.  For each tile the block
+//    The heads (64 rows of W each, 18 per KV head) are shared out over the 8
+//    XCDs as whole heads, and the 32 blocks of an XCD split its heads' rows
+//    into S K ranges (S = 4 for 8 KV heads, else 8) and row groups: block b
+//    owns one K range of 8192/S and 2 to 9 row tiles of 16 W rows, so every
+//    partial it produces is read on its own XCD.  For each tile the block
 //      - loads the 16 rows with non-temporal 16-byte loads, each wave
 //        instruction reading 1 KB of one row (the shape HBM streams best),
 //        several tiles ahead of use, into registers;
@@ -31,15 +34,15 @@
 //    and of the token's K|V slot.
 //
 //  No read-modify-write atomics, no flags, no counters and no cache
-//  maintenance.  Between calls every partial word holds kPartialEmpty (a NaN
+//  maintenance; every hand-off stays inside one XCD's L2.  Between calls every partial word holds kPartialEmpty (a NaN
 //  pattern no partial takes: a partial with those bits is stored as the
 //  canonical NaN), so a word that is not empty holds this call's partial:
 //  each word has one producer and one reader per call, and the reader
 //  empties it after use, so every call leaves the workspace as it found it.
-//  A partial read on the producing XCD is stored plainly into that XCD's L2;
-//  one read on another XCD is written through (device-coherent, agent
-//  scope).  The sums run in a fixed order, so the result depends on the
-//  launch shape only.
+//  Partials are stored plainly into the XCD's L2 (written through, device-
+//  coherent, only if the device did not place blocks on XCDs round robin).
+//  The sums run in a fixed order, so the result depends on the launch shape
+//  only.
 //
 //  A wave that waits too long sets the workspace's fault word and stores
 //  nothing; from then on every call finds the fault word set and runs no
@@ -80,25 +83,23 @@ constexpr float kEps = 1e-6f;
 template <int NKV>
 struct Shape {
     static constexpr int N = cols_for(NKV);
-    static constexpr int S = splits_for(NKV);      // K splits across blocks
-    static constexpr int KB = kHidden / S;         // K per block: 256 * NKV
-    static constexpr int KW = KB / kWaves;         // K per wave: 32 * NKV
+    static constexpr int HEADS = N / kHeadDim;     // 18 per KV head
+    static constexpr int S = NKV == 8 ? 4 : 8;     // K splits across blocks
+    static constexpr int KB = kHidden / S;         // K per block
+    static constexpr int KW = KB / kWaves;         // K per wave
     static constexpr int STEPS = KW / 32;          // MFMA K steps per tile and wave
-    static constexpr int GROUPS = kGrid / S;       // row groups of 9 tiles
     static constexpr int CHUNKS = KB / 8;          // 16-byte chunks per tile row
     static constexpr int LOADS = 2 * CHUNKS / 64;  // 1 KB loads per wave per tile (2 rows)
     static constexpr int TILE_BYTES = kTileRows * KB * 2;
-    // Double-buffered tile; for NKV <= 2 also the wave partials of all 9
-    // tiles, summed after the loop in the same LDS.
-    static constexpr int ALL_PARTIALS = 4 * kTilesPerBlock * kWaves * kTileRows * (kTileRows + 1);
-    static constexpr int LDS_BYTES =
-        NKV >= 4 || 2 * TILE_BYTES >= ALL_PARTIALS ? 2 * TILE_BYTES : ALL_PARTIALS;
-    // Tiles of loads in flight per wave: up to 12 loads of 1 KB per wave.
-    static constexpr int DEPTH = (12 / LOADS) < kTilesPerBlock ? (12 / LOADS) : kTilesPerBlock;
-    static_assert(S * GROUPS == kGrid, "grid covers every (split, group)");
-    static_assert(GROUPS * kTilesPerBlock * kTileRows == N, "groups cover N");
+    static constexpr int LDS_BYTES = 2 * TILE_BYTES;
+    // XCD x owns heads [x HEADS / 8, (x + 1) HEADS / 8); its 32 blocks take
+    // the S splits of 32 / S row groups of those heads' tiles.
+    static constexpr int MAX_HEADS = (HEADS + 7) / 8;
+    static constexpr int U_MAX = MAX_HEADS * 4 * S / 32;   // tiles per block, at most
+    static constexpr int DEPTH = (12 / LOADS) < U_MAX ? (12 / LOADS) : U_MAX;
     static_assert(KW % 32 == 0 && CHUNKS % 16 == 0, "whole MFMA steps, whole swizzle groups");
     static_assert(LOADS * 64 == 2 * CHUNKS, "each wave loads exactly two tile rows");
+    static_assert((HEADS / 8) * 4 * S % 32 == 0 && MAX_HEADS * 4 * S % 32 == 0, "whole tiles per block");
 };
 
 __device__ inline bf16x8 load16(const __bf16 *p)
@@ -130,7 +131,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             unsigned spin_limit)
 {
     using Sh = Shape<NKV>;
-    constexpr int ST = Sh::STEPS, D = Sh::DEPTH, U = kTilesPerBlock, C = Sh::CHUNKS;
+    constexpr int ST = Sh::STEPS, D = Sh::DEPTH, U = Sh::U_MAX, C = Sh::CHUNKS;
     constexpr int LD = Sh::LOADS, N = Sh::N, NQ = kQPerKv * NKV;
     constexpr size_t kTileStride = size_t(kTileRows) * kHidden;
     __shared__ __attribute__((aligned(16))) unsigned char lds[Sh::LDS_BYTES];
@@ -139,26 +140,30 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     const int b = blockIdx.x;
     // Blocks are dispatched to the 8 XCDs round robin: block b runs on XCD
     // (b + c) % 8 for a c that varies between launches.  So the 32 blocks
-    // with b % 8 == x share one XCD; they take the S splits of row groups
-    // x*NKV .. x*NKV + NKV - 1, rows [144 NKV x, 144 NKV (x + 1)), and the
-    // partials of a head stay in that XCD's L2 (for NKV >= 4 every head; for
-    // smaller NKV heads can straddle two XCDs).
+    // with b % 8 == x share one XCD; they own heads [x H / 8, (x + 1) H / 8)
+    // (H = 18 NKV heads: 2 or 3 heads each for NKV = 1, 4 or 5 for NKV = 2,
+    // 9 and 18 for NKV = 4 and 8) and take the S splits of 32 / S row groups
+    // of those heads' 16-row tiles, so the partials of a head never leave
+    // that XCD's L2.  Blocks of an XCD with more heads have more tiles: for
+    // NKV <= 2 that costs less than a hand-off between XCDs (measured: C1
+    // 8.41 -> 7.50 us, M = 16 at NKV = 1 9.61 -> 8.00 us, C2 10.17 -> 9.56 us
+    // against heads that straddle two XCDs with S = 32 / NKV).
     const int xcd = b & 7;
     const int slot_in_xcd = b >> 3;
     const int split = slot_in_xcd % Sh::S;
-    const int group = xcd * NKV + slot_in_xcd / Sh::S;
+    const int head_lo = xcd * Sh::HEADS / 8, head_hi = (xcd + 1) * Sh::HEADS / 8;
+    // tiles of this block: a constant when every XCD has as many heads
+    const int ub = Sh::HEADS % 8 == 0 ? Sh::U_MAX : (head_hi - head_lo) * Sh::S / 8;
+    const int tile0 = head_lo * 4 + (slot_in_xcd / Sh::S) * ub;   // its first 16-row tile
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;   // A row (W row in the tile) and B column (token)
     const int q = lane >> 4;   // which 8 of the 32 K values of a step
     const int k0 = split * Sh::KB;
-    constexpr int XCD_ROWS = N / 8;  // rows of W whose partials one XCD produces
 
     // This wave's epilogue item, if any: head `head` for tokens 2 tp (lanes
-    // 0-31) and 2 tp + 1 (lanes 32-63), among the heads whose first row lies
-    // in this XCD's rows; lane pi of each half owns rotation pair pi.
-    const int head_lo = (XCD_ROWS * xcd + kHeadDim - 1) / kHeadDim;
-    const int head_hi = (XCD_ROWS * (xcd + 1) + kHeadDim - 1) / kHeadDim;
+    // 0-31) and 2 tp + 1 (lanes 32-63), among this XCD's heads; lane pi of
+    // each half owns rotation pair pi.
     const int tpairs = (M + 1) >> 1;
     const int item = wave * (kGrid / 8) + slot_in_xcd;
     const bool has_item = item < (head_hi - head_lo) * tpairs;
@@ -197,7 +202,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     static_assert(size_t(N) * kHidden * 2 < (size_t(1) << 31), "W offsets fit 31 bits");
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(W), 0, int(size_t(N) * kHidden * 2), kBufferConfig);
-    const int wtile = int((size_t(group * U * kTileRows) * kHidden + k0) * 2);
+    const int wtile = int((size_t(tile0 * kTileRows) * kHidden + k0) * 2);
     constexpr int kTileBytes = int(kTileStride * 2);
     int goff[LD];
     int loff[LD];
@@ -212,10 +217,13 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
 
     bf16x8 ring[D][LD];
 #pragma unroll
-    for (int u = 0; u < D; ++u)
+    for (int u = 0; u < D; ++u) {
+        if (u < ub) {
 #pragma unroll
-        for (int j = 0; j < LD; ++j)
-            ring[u][j] = stream16(wr, wtile + u * kTileBytes + goff[j]);
+            for (int j = 0; j < LD; ++j)
+                ring[u][j] = stream16(wr, wtile + u * kTileBytes + goff[j]);
+        }
+    }
     if constexpr (NKV != 1)
         load_x();
 
@@ -243,14 +251,11 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     auto store_partial = [&](float sum, int u, int t, int row) {
         unsigned bits = __float_as_uint(sum);
         bits = bits == kPartialEmpty ? kPartialNan : bits;
-        const int n = (group * U + u) * kTileRows + row;
+        const int n = (tile0 + u) * kTileRows + row;
         unsigned *dst = parts + (size_t(split) * M + t) * N + n;
-        // The reader of row n runs on the XCD holding its head's first row.
-        // On this XCD a plain store is enough (the reader's device-coherent
-        // load is served by the shared L2); for another XCD the store writes
-        // through to memory.
-        const int reader_xcd = (n / kHeadDim) * kHeadDim / XCD_ROWS;
-        if (!coherent && reader_xcd == xcd)
+        // The reader of row n runs on this XCD: a plain store is enough (the
+        // reader's device-coherent load is served by the shared L2).
+        if (!coherent)
             *dst = bits;
         else
             __hip_atomic_store(dst, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -267,27 +272,25 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // tiles keep the loop short and reduce all tiles after it.  Lane (r, q)
     // holds D[row = 4q + v][token = r], v = 0..3; token columns r >= M are
     // never needed.
-    constexpr bool kReduceInLoop = NKV >= 4;
-    __shared__ float red[kReduceInLoop ? 2 : 1][kReduceInLoop ? SLAB : 1];
-    f32x4 acc[kReduceInLoop ? 1 : U];
+    __shared__ float red[2][SLAB];
     const bool summer = threadIdx.x < kTileRows * M;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+        if (u >= ub)
+            break;
         unsigned char *tile = lds + (u & 1) * Sh::TILE_BYTES;
 #pragma unroll
         for (int j = 0; j < LD; ++j)
             *reinterpret_cast<bf16x8 *>(tile + loff[j]) = ring[u % D][j];
-        if (u + D < U) {
+        if (u + D < ub) {
 #pragma unroll
             for (int j = 0; j < LD; ++j)
                 ring[u % D][j] = stream16(wr, wtile + (u + D) * kTileBytes + goff[j]);
         }
         __syncthreads();
-        if constexpr (kReduceInLoop) {
-            if (u > 0 && summer)
-                store_partial(block_sum(red[(u - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
-                              u - 1, threadIdx.x >> 4, threadIdx.x & 15);
-        }
+        if (u > 0 && summer)
+            store_partial(block_sum(red[(u - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
+                          u - 1, threadIdx.x >> 4, threadIdx.x & 15);
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < ST; ++st) {
@@ -295,41 +298,16 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const bf16x8 w = *reinterpret_cast<const bf16x8 *>(tile + (r * C + (c ^ r)) * 16);
             a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xv[st], a, 0, 0, 0);
         }
-        if constexpr (kReduceInLoop) {
-            if (r < M) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    red[u & 1][(wave * kTileRows + r) * (kTileRows + 1) + 4 * q + v] = a[v];
-            }
-        } else {
-            acc[u] = a;
-        }
-    }
-    if constexpr (kReduceInLoop) {
-        __syncthreads();
-        if (summer)
-            store_partial(block_sum(red[(U - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
-                          U - 1, threadIdx.x >> 4, threadIdx.x & 15);
-    } else {
-        // All tiles at once, in the tile buffers the loop no longer needs.
-        float *all = reinterpret_cast<float *>(lds);
-        static_assert(sizeof(float) * U * SLAB <= Sh::LDS_BYTES, "partials fit in LDS");
-        __syncthreads();
         if (r < M) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    all[u * SLAB + (wave * kTileRows + r) * (kTileRows + 1) + 4 * q + v] = acc[u][v];
-        }
-        __syncthreads();
-        const int per_tile = kTileRows * M;
-        for (int e = threadIdx.x; e < U * per_tile; e += kWaves * 64) {
-            const int u = e / per_tile;
-            const int rem = e - u * per_tile;
-            store_partial(block_sum(all + u * SLAB, rem >> 4, rem & 15), u, rem >> 4, rem & 15);
+            for (int v = 0; v < 4; ++v)
+                red[u & 1][(wave * kTileRows + r) * (kTileRows + 1) + 4 * q + v] = a[v];
         }
     }
+    __syncthreads();
+    if (summer)
+        store_partial(block_sum(red[(ub - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
+                      ub - 1, threadIdx.x >> 4, threadIdx.x & 15);
 
     // A device left in the fault state by an earlier call: no reader runs,
     // so no y or cache entry is stored (partials stored above are emptied
@@ -348,20 +326,6 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         const int split_bytes = M * N * int(sizeof(unsigned));
         // One 8-byte load per split reads the two columns' words; each word
         // was stored whole and is checked on its own.
-        // With NKV = 1 a full round reads 32 splits x 8 bytes per lane, so the
-        // wave first polls lightly: lane pi watches one word (its first column
-        // in split pi % S) until every lane's word is full; the full read
-        // below still checks every word.  (Measured faster for NKV = 1 only.)
-        if constexpr (NKV == 1) {
-            for (unsigned tries = 0;; ++tries) {
-                asm volatile("" ::: "memory");
-                const unsigned w0 = __builtin_amdgcn_raw_buffer_load_b32(
-                    rsrc, base + (pi % Sh::S) * split_bytes, 0, kCacheSc1);
-                if (__all(w0 != kPartialEmpty) || tries >= spin_limit)
-                    break;
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
         u32x2 v[Sh::S];
         bool gave_up = false;
         for (unsigned tries = 0;; ++tries) {

@@ -57,10 +57,16 @@ def test_plan_is_a_function_of_shape(L, nkv):
     N = qf.n_cols(nkv)
     for M in (1, 8, 16):
         p = qf.plan(N, M)
-        assert p == {"grid": 256, "k_splits": 32 // nkv, "waves_per_block": 8,
-                     "tiles_per_block": 9}
+        S = 4 if nkv == 8 else 8
+        H = N // 64
+        heads = [(x + 1) * H // 8 - x * H // 8 for x in range(8)]
+        tiles = [h * 4 * S // 32 for h in heads]       # per block on XCD x
+        assert all(h * 4 * S % 32 == 0 for h in heads)
+        assert p == {"grid": 256, "k_splits": S, "waves_per_block": 8,
+                     "tiles_per_block": max(tiles)}
         # every W row tile and every K split is covered exactly once
-        assert p["grid"] * p["tiles_per_block"] == (N // 16) * p["k_splits"]
+        assert sum(32 * t for t in tiles) == (N // 16) * S
+        assert max(tiles) == {1: 3, 2: 5, 4: 9, 8: 9}[nkv]
 
 
 def test_plan_rejects_bad_shapes(L):
