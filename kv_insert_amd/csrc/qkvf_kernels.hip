@@ -116,6 +116,29 @@ __device__ inline bf16x8 stream16(__amdgpu_buffer_rsrc_t w, int off)
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// A lane's value moved by a DPP control code within its row of 16 lanes.
+template <int CTRL>
+__device__ inline float dpp_move(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The sum of v over each half-wave (lanes 0-31, 32-63), in every lane of
+// it: quad swaps, then the 8-lane and 16-lane mirrors (DPP, no LDS), then
+// one swizzle that exchanges the two rows of 16 (lane ^ 16).  Each step adds
+// two equal-sized partial sums, so every lane of the half ends with the same
+// bits.
+__device__ inline float half_wave_sum(float v)
+{
+    v += dpp_move<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_move<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_move<0x141>(v);   // row_half_mirror
+    v += dpp_move<0x140>(v);   // row_mirror
+    // ds_swizzle bit mode within 32 lanes: and 0x1F, or 0, xor 0x10
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    return v;
+}
+
 __device__ inline unsigned pack2(__bf16 lo, __bf16 hi)
 {
     return unsigned(__builtin_bit_cast(unsigned short, lo)) |
@@ -369,12 +392,9 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         const __bf16 p0 = __bf16(a0), p1 = __bf16(a1);
         const float f0 = float(p0), f1 = float(p1);
 
-        // Sum of squares of the head's 64 values: butterfly over the 32 lanes
-        // of the half-wave (every lane ends with the same total).
-        float ss = f0 * f0 + f1 * f1;
-#pragma unroll
-        for (int m = 16; m >= 1; m >>= 1)
-            ss += __shfl_xor(ss, m, 64);
+        // Sum of squares of the head's 64 values over the 32 lanes of the
+        // half-wave (every lane ends with the same total).
+        const float ss = half_wave_sum(f0 * f0 + f1 * f1);
 
         if (cos_sin == nullptr) {  // a layer without RoPE: norm only
             rc = 1.f;
