@@ -73,6 +73,8 @@ def parse():
                     help="also time every workload and sweep point; one JSON line each on stderr")
     ap.add_argument("--attn2", default="", metavar="WORKLOAD",
                     help="time attn2 instead of the front: one of " + ", ".join(wl.ATTN2_WORKLOADS))
+    ap.add_argument("--attn2-batch-invariant", action="store_true",
+                    help="with --attn2: prepare the layer with batch-invariant splits")
     ap.add_argument("--layer-front", default="", metavar="WORKLOAD",
                     help="time LayerFront instead of the front: one of "
                          + ", ".join(wl.LAYER_FRONT_WORKLOADS))
@@ -274,10 +276,11 @@ def attn2_sets(a: wl.Attn2Workload) -> int:
     return max(a.sets, int(600e6 // kv) + 1)
 
 
-def time_attn2(a: wl.Attn2Workload, steps: int, warmup: int, repeats: int):
+def time_attn2(a: wl.Attn2Workload, steps: int, warmup: int, repeats: int,
+               invariant: bool = False):
     sets = attn2_sets(a)
     pool = Attn2Pool(a, sets)
-    qf.attn2_prepare(a.nkv, a.max_model_len, a.R, a.window)
+    qf.attn2_prepare(a.nkv, a.max_model_len, a.R, a.window, batch_invariant=invariant)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -328,10 +331,11 @@ def attn2_cpu_baseline(a: wl.Attn2Workload, budget_s: float) -> dict | None:
 
 
 def attn2_line(a: wl.Attn2Workload, args) -> dict:
-    ms, times, sets = time_attn2(a, args.steps, args.warmup, args.repeats)
+    invariant = bool(getattr(args, "attn2_batch_invariant", False))
+    ms, times, sets = time_attn2(a, args.steps, args.warmup, args.repeats, invariant)
     nbytes = a.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
-    z = qf.attn2_plan(a.nkv, a.max_model_len, a.window, a.R)
+    z = qf.attn2_plan(a.nkv, a.max_model_len, a.window, 1 if invariant else a.R)
     kernels = "attn2_split" + (" + attn2_merge" if z > 1 else "")
     return {
         "metric": "attn2 achieved HBM GB/s (algorithmic bytes per call / time per call)",
@@ -339,8 +343,8 @@ def attn2_line(a: wl.Attn2Workload, args) -> dict:
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": dict(wl.describe_attn2(a), splits=z, request_sets_rotated=sets,
-                       algorithmic_bytes_per_call=nbytes),
+        "config": dict(wl.describe_attn2(a), splits=z, batch_invariant_splits=invariant,
+                       request_sets_rotated=sets, algorithmic_bytes_per_call=nbytes),
         "roofline": {"bound": "hbm", "kernel": f"{kernels} (the whole call)",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -237,13 +237,30 @@ int qkvf_fault_word(unsigned **word);
  * least max_model_len is none) and sizes the device workspace in which
  * calls split their keys over several blocks (the split count depends on
  * these values and the call's request count only, see qkvf_attn2_plan, so
- * the launch shape of a batch size is fixed and capturable).  It may
+ * the launch shape of a batch size is fixed and capturable;
+ * qkvf_attn2_prepare_ex can fix it for every batch size).  It may
  * allocate; a workspace it outgrows stays allocated (a call already
  * launched may still use it) until qkvf_release.
  * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS (max_reqs outside [1, 64]),
  * QKVF_ERR_DEVICE, QKVF_ERR_ALLOC.
  */
 int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int window);
+
+/*
+ * qkvf_attn2_prepare with a choice of split count.  batch_invariant == 0 is
+ * qkvf_attn2_prepare: the split count follows the call's request count
+ * (about 256 blocks per launch), so a request's output may differ in its
+ * last bits (the fp32 summation order of its splits) with the number of
+ * requests it is batched with.  batch_invariant == 1: every call uses the
+ * split count of one request (qkvf_attn2_plan with num_reqs = 1), so a
+ * request's output bits depend only on its own inputs and the layer; a
+ * batch of R requests then launches R times that many blocks and sizes the
+ * workspace for it (R x the partials of one request).
+ * Errors: those of qkvf_attn2_prepare, and QKVF_ERR_RANGE for another
+ * batch_invariant value.
+ */
+int qkvf_attn2_prepare_ex(int num_kv_heads, int max_model_len, int max_reqs, int window,
+                          int batch_invariant);
 
 /*
  * Enqueue attn2 for num_reqs requests on `stream` (device pointers):
@@ -272,7 +289,8 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate,
                    const int32_t *seq_lens, int num_reqs, void *out,
                    int64_t out_row_stride, hipStream_t stream);
 
-/* The number of key splits attn2 uses for a layer and a request count: about
+/* The number of key splits attn2 uses for a layer and a request count (with
+ * batch-invariant splits, the count for num_reqs = 1 applies to every call): about
  * 256 / (num_reqs * num_kv_heads) blocks per request and KV head, at most
  * one per 128 keys of the span a request's rows attend (max_model_len, or
  * window + 7), at most 64; 1 means no merge pass.  A pure function of its

@@ -30,7 +30,7 @@ EXPORTS = ("qkvf_prepare", "qkvf_run", "qkvf_run_static", "qkvf_check", "qkvf_st
            "qkvf_workspace_bytes", "qkvf_set_handoff", "qkvf_set_spin_limit",
            "qkvf_device_fault", "qkvf_fault_word",
            "qkvf_release",
-           "qkvf_attn2_prepare", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front", "qkvf_route",
+           "qkvf_attn2_prepare", "qkvf_attn2_prepare_ex", "qkvf_attn2_run", "qkvf_attn2_plan", "qkvf_layer_front", "qkvf_route",
            "qkvf_stream_read")
 
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.qkvf_fault_word.restype = I
     L.qkvf_attn2_prepare.argtypes = [I, I, I, I]
     L.qkvf_attn2_prepare.restype = I
+    L.qkvf_attn2_prepare_ex.argtypes = [I, I, I, I, I]
+    L.qkvf_attn2_prepare_ex.restype = I
     L.qkvf_attn2_run.argtypes = [P, I64, P, I64, P, P, I64, P, I, P, I64, P]
     L.qkvf_attn2_run.restype = I
     L.qkvf_attn2_plan.argtypes = [I, I, I, I, P]
@@ -200,10 +202,14 @@ def release() -> None:
     lib().qkvf_release()
 
 
-def attn2_prepare(num_kv_heads: int, max_model_len: int, max_reqs: int, window: int = 0) -> None:
-    """qkvf_attn2_prepare: bind a layer's attn2 configuration to this thread."""
-    _raise(lib().qkvf_attn2_prepare(int(num_kv_heads), int(max_model_len), int(max_reqs),
-                                    int(window)), "qkvf_attn2_prepare")
+def attn2_prepare(num_kv_heads: int, max_model_len: int, max_reqs: int, window: int = 0,
+                  batch_invariant: bool = False) -> None:
+    """qkvf_attn2_prepare(_ex): bind a layer's attn2 configuration to this
+    thread; batch_invariant fixes the split count at one request's, so a
+    request's output does not depend on the rest of its batch."""
+    _raise(lib().qkvf_attn2_prepare_ex(int(num_kv_heads), int(max_model_len), int(max_reqs),
+                                       int(window), 1 if batch_invariant else 0),
+           "qkvf_attn2_prepare")
 
 
 def attn2_run(q, gate, kv_cache, block_table, seq_lens, out, stream=None) -> None:

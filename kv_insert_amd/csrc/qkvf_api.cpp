@@ -52,6 +52,7 @@ thread_local int t_nkv = 0;
 // attn2 configuration bound by the last qkvf_attn2_prepare of this thread.
 struct Attn2Config {
     int nkv = 0, max_model_len = 0, max_reqs = 0, window = 0;
+    bool invariant = false;   // split count of one request for every batch size
 };
 thread_local Attn2Config t_attn2;
 
@@ -318,7 +319,7 @@ const char *qkvf_strerror(int status)
     case QKVF_ERR_NOT_PREPARED: return "qkvf_prepare has not been called for this shape and row count on this thread and device";
     case QKVF_ERR_ALLOC: return "the device workspace could not be allocated";
     case QKVF_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    case QKVF_ERR_RANGE: return "a position or slot is out of range, or a slot repeats";
+    case QKVF_ERR_RANGE: return "a position or slot is out of range, a slot repeats, or a mode argument is not one of its values";
     case QKVF_ERR_OVERLAP: return "y or kv_cache overlaps another operand";
     case QKVF_ERR_MEMORY: return "a pointer is not device memory of the current device";
     case QKVF_ERR_TIMEOUT: return "a call on this device gave up waiting for a partial result (its blocks could not all run, or the device placed blocks on XCDs differently than at prepare); it and every call after it stored nothing until this report";
@@ -451,6 +452,14 @@ void qkvf_release(void)
 
 int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int window)
 {
+    return qkvf_attn2_prepare_ex(num_kv_heads, max_model_len, max_reqs, window, 0);
+}
+
+int qkvf_attn2_prepare_ex(int num_kv_heads, int max_model_len, int max_reqs, int window,
+                          int batch_invariant)
+{
+    if (batch_invariant != 0 && batch_invariant != 1)
+        return QKVF_ERR_RANGE;
     if (!valid_nkv(num_kv_heads) || max_model_len < 8 || window < 0)
         return QKVF_ERR_SHAPE;
     if (max_reqs < 1 || max_reqs > kAttn2MaxReqs)
@@ -463,7 +472,8 @@ int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int wi
     DeviceState &st = g_dev[dev];
     // A window that covers every position is no window.
     const int win = window >= max_model_len ? 0 : window;
-    const size_t need = attn2_workspace_floats(num_kv_heads, max_reqs, max_model_len, win);
+    const size_t need =
+        attn2_workspace_floats(num_kv_heads, max_reqs, max_model_len, win, batch_invariant == 1);
     if (need > st.attn2_ws_floats.load(std::memory_order_relaxed)) {
         void *p = nullptr;
         if (hipMalloc(&p, need * sizeof(float)) != hipSuccess) {
@@ -475,7 +485,7 @@ int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int wi
         if (old != nullptr)
             st.retired.push_back(old);
     }
-    t_attn2 = Attn2Config{num_kv_heads, max_model_len, max_reqs, win};
+    t_attn2 = Attn2Config{num_kv_heads, max_model_len, max_reqs, win, batch_invariant == 1};
     return QKVF_OK;
 }
 
@@ -503,7 +513,7 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate, int64_
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QKVF_ERR_DEVICE;
     const DeviceState &st = g_dev[dev];
-    const int z = attn2_splits(cfg.nkv, num_reqs, cfg.max_model_len, cfg.window);
+    const int z = attn2_splits(cfg.nkv, cfg.invariant ? 1 : num_reqs, cfg.max_model_len, cfg.window);
     const size_t need = z > 1 ? size_t(num_reqs) * cfg.nkv * z * 64 * kAttn2PartialFloats : 0;
     // Size first: a buffer published with this size or a later, larger one.
     if (need > st.attn2_ws_floats.load(std::memory_order_acquire))

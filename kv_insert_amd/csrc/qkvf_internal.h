@@ -109,7 +109,10 @@ static_assert(attn2_q_piece(3, 1) + 8 <= kHeadDim && attn2_q_piece(0, 0) >= 0,
 // there are at most 64.
 // The count depends on the deployment and the batch size, not on the step's
 // lengths, so the launch shape is fixed for a captured batch size; shorter
-// contexts leave the trailing splits empty.
+// contexts leave the trailing splits empty.  A layer prepared with
+// batch-invariant splits uses the one-request count for every batch size, so
+// a request's output bits do not depend on the other requests of its batch
+// (at the price of more blocks and partials for larger batches).
 constexpr int kAttn2TargetBlocks = 256;
 constexpr int kAttn2MinSplitKeys = 128;
 constexpr int kAttn2MaxSplits = 64;
@@ -132,12 +135,14 @@ inline int attn2_splits(int nkv, int num_reqs, int max_model_len, int window)
     return z < 2 ? 1 : z;
 }
 
-// Workspace floats for every batch size up to max_reqs.
-inline size_t attn2_workspace_floats(int nkv, int max_reqs, int max_model_len, int window)
+// Workspace floats for every batch size up to max_reqs (with batch-invariant
+// splits every batch uses the one-request split count).
+inline size_t attn2_workspace_floats(int nkv, int max_reqs, int max_model_len, int window,
+                                     bool invariant = false)
 {
     size_t most = 0;
     for (int r = 1; r <= max_reqs; ++r) {
-        const int z = attn2_splits(nkv, r, max_model_len, window);
+        const int z = attn2_splits(nkv, invariant ? 1 : r, max_model_len, window);
         const size_t n = z > 1 ? size_t(r) * nkv * z * 64 * kAttn2PartialFloats : 0;
         if (n > most)
             most = n;

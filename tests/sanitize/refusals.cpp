@@ -102,6 +102,9 @@ int main()
     expect("attn2 prepare window", qkvf_attn2_prepare(8, 4096, 1, -1), 2);
     expect("attn2 prepare reqs", qkvf_attn2_prepare(8, 4096, 65, 0), 3);
     expect("attn2 prepare device", qkvf_attn2_prepare(8, 4096, 1, 0), 1);
+    expect("attn2 prepare_ex mode", qkvf_attn2_prepare_ex(8, 4096, 1, 0, 2), 9);
+    expect("attn2 prepare_ex nkv", qkvf_attn2_prepare_ex(3, 4096, 1, 0, 1), 2);
+    expect("attn2 prepare_ex device", qkvf_attn2_prepare_ex(8, 4096, 64, 0, 1), 1);
     expect("attn2 run unprepared",
            qkvf_attn2_run(P, 4096, P, 4096, P, pi32, 1, pi32, 1, P, 4096, nullptr), 6);
     for (int nkv : {1, 2, 4, 8})

@@ -186,6 +186,13 @@ def test_attn2_prepare_rejects_bad_shapes_before_the_device(L, nkv, mml, reqs, w
     assert L.qkvf_attn2_plan(nkv, mml, max(window, 0), 1, None) in (0, 2)
 
 
+def test_attn2_prepare_ex_refuses_an_unknown_mode(L):
+    assert L.qkvf_attn2_prepare_ex(8, 4096, 1, 0, 2) == 9
+    assert L.qkvf_attn2_prepare_ex(8, 4096, 1, 0, -1) == 9
+    assert L.qkvf_attn2_prepare_ex(3, 4096, 1, 0, 1) == 2
+    assert L.qkvf_attn2_prepare_ex(8, 4096, 65, 0, 1) == 3
+
+
 def test_attn2_run_without_prepare_is_refused(L):
     res = []
 
