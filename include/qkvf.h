@@ -235,10 +235,10 @@ int qkvf_fault_word(unsigned **word);
  * qkvf_attn2_prepare binds a layer's (num_kv_heads, max_model_len,
  * max_reqs, window) to the calling thread (window 0: none; a window of at
  * least max_model_len is none) and sizes the device workspace in which
- * calls split their keys over several blocks (the split count depends on
+ * calls split their keys over several blocks (the launch shape depends on
  * these values and the call's request count only, see qkvf_attn2_plan, so
- * the launch shape of a batch size is fixed and capturable;
- * qkvf_attn2_prepare_ex can fix it for every batch size).  It may
+ * it is fixed for a batch size and capturable; qkvf_attn2_prepare_ex can
+ * fix each request's split count for every batch size).  It may
  * allocate; a workspace it outgrows stays allocated (a call already
  * launched may still use it) until qkvf_release.
  * Errors: QKVF_ERR_SHAPE, QKVF_ERR_ROWS (max_reqs outside [1, 64]),
@@ -248,14 +248,14 @@ int qkvf_attn2_prepare(int num_kv_heads, int max_model_len, int max_reqs, int wi
 
 /*
  * qkvf_attn2_prepare with a choice of split count.  batch_invariant == 0 is
- * qkvf_attn2_prepare: the split count follows the call's request count
- * (about 256 blocks per launch), so a request's output may differ in its
- * last bits (the fp32 summation order of its splits) with the number of
- * requests it is batched with.  batch_invariant == 1: every call uses the
- * split count of one request (qkvf_attn2_plan with num_reqs = 1), so a
- * request's output bits depend only on its own inputs and the layer; a
- * batch of R requests then launches R times that many blocks and sizes the
- * workspace for it (R x the partials of one request).
+ * qkvf_attn2_prepare: the requests of a call share its split slots (about
+ * 256 blocks per launch) in proportion to their lengths, so a request's
+ * output may differ in its last bits (the fp32 summation order of its
+ * splits) with the requests it is batched with.  batch_invariant == 1: every
+ * request takes the split count of one request alone (qkvf_attn2_plan with
+ * num_reqs = 1), so a request's output bits depend only on its own inputs
+ * and the layer; a batch of R requests then launches R times that many
+ * blocks and sizes the workspace for it (R x the partials of one request).
  * Errors: those of qkvf_attn2_prepare, and QKVF_ERR_RANGE for another
  * batch_invariant value.
  */
@@ -289,12 +289,17 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate,
                    const int32_t *seq_lens, int num_reqs, void *out,
                    int64_t out_row_stride, hipStream_t stream);
 
-/* The number of key splits attn2 uses for a layer and a request count (with
- * batch-invariant splits, the count for num_reqs = 1 applies to every call): about
- * 256 / (num_reqs * num_kv_heads) blocks per request and KV head, at most
- * one per 128 keys of the span a request's rows attend (max_model_len, or
- * window + 7), at most 64; 1 means no merge pass.  A pure function of its
- * arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or QKVF_ERR_ROWS. */
+/* The split slots per KV head of an attn2 launch for a layer and a request
+ * count: ceil(256 / num_kv_heads) (about one 16-wave block per CU), capped
+ * by num_reqs times the splits one request can take (one per 128 keys of the
+ * span its rows attend, max_model_len or window + 7, and at most 64); 1 when
+ * that is not more than num_reqs, meaning every request takes one split and
+ * there is no merge pass.  The requests of a call share the slots: one split
+ * length for the call, the shortest whole number of 128-key steps for which
+ * every request's splits fit, so a request's split count follows its length.
+ * With num_reqs = 1 it is the request's split count, which batch-invariant
+ * splits use for every request.  A pure function of its arguments.
+ * Returns QKVF_OK, QKVF_ERR_SHAPE or QKVF_ERR_ROWS. */
 int qkvf_attn2_plan(int num_kv_heads, int max_model_len, int window, int num_reqs,
                     int *splits);
 

@@ -224,8 +224,9 @@ def attn2_run(q, gate, kv_cache, block_table, seq_lens, out, stream=None) -> Non
 
 
 def attn2_plan(num_kv_heads: int, max_model_len: int, window: int = 0, num_reqs: int = 1) -> int:
-    """qkvf_attn2_plan: the number of key splits of a launch for num_reqs
-    requests (1: no merge pass)."""
+    """qkvf_attn2_plan: the split slots per KV head of a launch for num_reqs
+    requests, which the requests share in proportion to their lengths (with
+    num_reqs = 1: the request's split count; 1: no merge pass)."""
     z = ctypes.c_int()
     _raise(lib().qkvf_attn2_plan(int(num_kv_heads), int(max_model_len), int(window),
                                  int(num_reqs), ctypes.byref(z)), "qkvf_attn2_plan")

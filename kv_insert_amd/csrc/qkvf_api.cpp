@@ -513,15 +513,16 @@ int qkvf_attn2_run(const void *q, int64_t q_row_stride, const void *gate, int64_
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QKVF_ERR_DEVICE;
     const DeviceState &st = g_dev[dev];
-    const int z = attn2_splits(cfg.nkv, cfg.invariant ? 1 : num_reqs, cfg.max_model_len, cfg.window);
-    const size_t need = z > 1 ? size_t(num_reqs) * cfg.nkv * z * 64 * kAttn2PartialFloats : 0;
+    const Attn2Launch l =
+        attn2_launch(cfg.nkv, num_reqs, cfg.max_model_len, cfg.window, cfg.invariant);
+    const size_t need = attn2_call_floats(l, cfg.nkv, num_reqs);
     // Size first: a buffer published with this size or a later, larger one.
     if (need > st.attn2_ws_floats.load(std::memory_order_acquire))
         return QKVF_ERR_NOT_PREPARED;
     float *ws = st.attn2_ws.load(std::memory_order_acquire);
     const hipError_t e = launch_attn2(q, q_row_stride, gate, gate_row_stride, kv_cache, cfg.nkv,
                                       block_table, block_table_stride, seq_lens, num_reqs,
-                                      cfg.max_model_len, cfg.window, z, ws, out, out_row_stride,
+                                      cfg.max_model_len, cfg.window, l, ws, out, out_row_stride,
                                       stream);
     return e == hipSuccess ? QKVF_OK : QKVF_ERR_HIP;
 }

@@ -31,10 +31,14 @@
 //                 B = the lane's 8 weights as bf16 hi + lo parts, so no lane
 //                 exchange is needed and the weights keep ~16 bits); the row
 //                 sums come from the same parts through an all-ones A operand.
-// After the loop the 4 key groups merge in LDS.  With one split the block
-// finishes its rows itself; otherwise it writes (max, sum, O) per row to the
-// workspace and attn2_merge, one wave per output row, combines the splits in
-// split order, then applies the norm and the gate.
+// After the loop the 4 key groups merge in LDS.  A request with one split
+// has its rows finished by that block; otherwise each block writes (max,
+// sum, O) per row to the workspace and attn2_merge, one wave per output row,
+// combines the request's splits in split order, then applies the norm and
+// the gate.  Blocks find their (request, split) either from the grid (one
+// set of splits per request) or, when the requests share the launch's split
+// slots, from all requests' lengths (shared_geometry below), which the merge
+// works out again for itself.
 #include <hip/hip_runtime.h>
 
 #include "qkvf_internal.h"
@@ -96,27 +100,134 @@ __device__ inline Geom split_geom(int L, int window, int Z)
     return g;
 }
 
+// Inclusive prefix sum (OP = +) or prefix max over the wave's 64 lanes of
+// non-negative values: shifts by 1, 2, 4 and 8 lanes within each row of 16
+// (lanes without a source add 0), then row 0's last lane into row 1 and row
+// 2's into row 3, then lane 31 into rows 2 and 3.  Lane 63 ends with the
+// total.
+template <int CTRL, int ROWS = 0xF>
+__device__ inline int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+
+template <bool MAX>
+__device__ inline int wave_scan_i(int v)
+{
+    auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };
+    v = op(v, dpp_i<0x111>(v));         // row_shr:1
+    v = op(v, dpp_i<0x112>(v));         // row_shr:2
+    v = op(v, dpp_i<0x114>(v));         // row_shr:4
+    v = op(v, dpp_i<0x118>(v));         // row_shr:8
+    v = op(v, dpp_i<0x142, 0xA>(v));    // row_bcast:15 into rows 1 and 3
+    v = op(v, dpp_i<0x143, 0xC>(v));    // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+__device__ inline int wave_sum_i(int v) { return __builtin_amdgcn_readlane(wave_scan_i<false>(v), 63); }
+__device__ inline int wave_max_i(int v) { return __builtin_amdgcn_readlane(wave_scan_i<true>(v), 63); }
+
+// Chunks a request attends from the page of its earliest key (>= 1).
+__device__ inline int request_chunks(int L, int window)
+{
+    const int lo0 = window > 0 ? max(0, L - 8 - window + 1) : 0;
+    return (L - (lo0 & ~(kPageSlots - 1)) + kChunk - 1) / kChunk;
+}
+
+// Geometry of a launch whose R requests share Z > R split slots per KV
+// head.  The split length `per` (chunks) is the shortest whole number of
+// steps, at least kMinSplitChunks and at least 1 / kAttn2MaxSplits of the
+// longest request, for which the requests' splits, ceil(c / per) each, fit
+// in Z.  The count of splits only falls as the length grows, and at the
+// longest request's length every request takes one split (R < Z), so a
+// bisection over whole steps finds it; most launches stop at the first try.
+// Request r's splits are the slots [off_r, off_r + nz_r) in request order.
+// Every lane returns per; lane l < R also request l's length, nz and off.
+struct SharedGeom {
+    int per, L, nz, off;
+};
+
+__device__ inline SharedGeom shared_geometry(const int32_t *seq_lens, int R, int max_len,
+                                             int window, int Z, int lane)
+{
+    SharedGeom g;
+    g.L = lane < R ? min(max(seq_lens[lane], 8), max_len) : 8;
+    const int c = lane < R ? request_chunks(g.L, window) : 0;
+    const int total = wave_sum_i(c), most = wave_max_i(c);
+    auto up = [](int v) { return (v + kGroups - 1) / kGroups * kGroups; };
+    int lo = up(max(max((total + Z - 1) / Z, kMinSplitChunks),
+                    (most + kAttn2MaxSplits - 1) / kAttn2MaxSplits));
+    g.per = lo;
+    g.nz = (c + lo - 1) / lo;
+    if (wave_sum_i(g.nz) > Z) {
+        // Some request is longer than lo (else every request has one split,
+        // R < Z): at hi = its length, R splits fit.
+        int hi = up(most);
+        while (hi - lo > kGroups) {
+            const int mid = lo + (hi - lo) / (2 * kGroups) * kGroups;
+            if (wave_sum_i((c + mid - 1) / mid) <= Z)
+                hi = mid;
+            else
+                lo = mid;
+        }
+        g.per = hi;
+        g.nz = (c + hi - 1) / hi;
+    }
+    g.off = wave_scan_i<false>(g.nz) - g.nz;
+    return g;
+}
+
+// Reductions of floats over the 16 lanes of a DPP row (every lane of the
+// row gets the result): swap neighbours, swap pairs, mirror the half rows,
+// mirror the row.  Over the wave, the four rows' results combine in a fixed
+// order.
+template <int CTRL>
+__device__ inline float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ inline float row_sum(float v)
+{
+    v += dpp_f<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x141>(v);   // row_half_mirror
+    v += dpp_f<0x140>(v);   // row_mirror
+    return v;
+}
+
+__device__ inline float row_max(float v)
+{
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return v;
+}
+
+__device__ inline float lane_f(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 __device__ inline float wave_max(float v)
 {
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1)
-        v = fmaxf(v, __shfl_xor(v, k, 64));
-    return v;
+    v = row_max(v);
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 __device__ inline float wave_sum(float v)
 {
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1)
-        v += __shfl_xor(v, k, 64);
-    return v;
+    v = row_sum(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
+template <bool SHARED>
 __global__ void __launch_bounds__(kThreads)
 attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__restrict__ gate,
             int64_t gate_stride, const __bf16 *__restrict__ kv_cache, int nkv,
             const int32_t *__restrict__ block_table, int64_t bt_stride,
-            const int32_t *__restrict__ seq_lens, int max_len, int window, int Z,
+            const int32_t *__restrict__ seq_lens, int R, int max_len, int window, int Z,
             float *__restrict__ ws, __bf16 *__restrict__ out, int64_t out_stride)
 {
     // Two step buffers of K [128 keys][64] and V [128 keys][64];
@@ -125,8 +236,53 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
     __shared__ int64_t pg[kSegPages];   // element offset of each page's K|V rows
     __shared__ float2 ml_lds[kGroups][64];
 
-    const int z = blockIdx.x, j = blockIdx.y, r = blockIdx.z;
+    const int j = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
+    // This block's request r, its split z, the request's length and geometry,
+    // and the index f of the block's partial among a KV head's partials.
+    int r, z, L, f;
+    Geom geo;
+    if constexpr (!SHARED) {
+        r = blockIdx.z;
+        z = blockIdx.x;
+        f = r * Z + z;
+        // A length outside [8, max_len] breaks the caller's contract; clamping
+        // it keeps the block-table reads inside the rows the caller sized.
+        L = min(max(seq_lens[r], 8), max_len);
+        geo = split_geom(L, window, Z);
+    } else {
+        // Wave 0 works the launch's geometry out from all the lengths and
+        // hands this block's part to the others through LDS.
+        __shared__ int plan_lds[5];
+        f = blockIdx.x;
+        if (tid < 64) {
+            const SharedGeom sg = shared_geometry(seq_lens, R, max_len, window, Z, lane);
+            const uint64_t mine =
+                __builtin_amdgcn_ballot_w64(lane < R && f >= sg.off && f < sg.off + sg.nz);
+            const int rr = mine != 0 ? __builtin_ctzll(mine) : -1;
+            const int k = rr < 0 ? 0 : rr;
+            const int zk = f - __builtin_amdgcn_readlane(sg.off, k);
+            const int Lk = __builtin_amdgcn_readlane(sg.L, k);
+            const int nzk = __builtin_amdgcn_readlane(sg.nz, k);
+            if (lane == 0) {
+                plan_lds[0] = rr;
+                plan_lds[1] = zk;
+                plan_lds[2] = Lk;
+                plan_lds[3] = sg.per;
+                plan_lds[4] = nzk;
+            }
+        }
+        __syncthreads();
+        r = plan_lds[0];
+        if (r < 0)
+            return;   // a slot past the last split (uniform over the block)
+        z = plan_lds[1];
+        L = plan_lds[2];
+        geo.lo0 = window > 0 ? max(0, L - 8 - window + 1) : 0;
+        geo.base = geo.lo0 & ~(kPageSlots - 1);
+        geo.per = plan_lds[3];
+        geo.nz = plan_lds[4];
+    }
     const int grp = tid >> 8;                  // key group: keys 32 grp .. of a step
     const int wq = (tid >> 6) & 3;             // query wave within the group
     const int c = lane & 15;   // query row of the wave (B column / output column)
@@ -135,19 +291,25 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
     const int t = c & 7;                       // token of the row
     const int head = kQPerKv * j + hh;         // q head index in the row
     const int64_t row = int64_t(r) * 8 + t;
-    // A length outside [8, max_len] breaks the caller's contract; clamping it
-    // keeps the block-table reads inside the rows the caller sized.
-    const int L = min(max(seq_lens[r], 8), max_len);
     const int pos = L - 8 + t;
     const int lo = window > 0 ? max(0, pos - window + 1) : 0;
     const int lo_last = window > 0 ? max(0, L - window) : 0;   // lo of token 7
     const float sc = 0.125f * kLog2e;          // softmax scale, in log2 units
 
-    const Geom geo = split_geom(L, window, Z);
     if (z >= geo.nz)
         return;   // nothing to attend in this split; the merge skips it
     const int first = geo.base + z * geo.per * kChunk;
     const int end = min(L, first + geo.per * kChunk);
+
+    // After the key loop thread tid combines query cq = tid / 16, dims
+    // d0 .. d0 + 3; a request with one split finishes its rows here, so its
+    // gate values are fetched now, while the keys stream.
+    const int cq = tid >> 4, d0 = 4 * (tid & 15);
+    const int64_t crow = int64_t(r) * 8 + (cq & 7);                       // token cq % 8
+    const int64_t ccol = int64_t(kQPerKv * j + (cq >> 3)) * kHeadDim + d0; // q head cq / 8
+    bf16x4 gv = {};
+    if (geo.nz == 1)
+        gv = *reinterpret_cast<const bf16x4 *>(gate + crow * gate_stride + ccol);
 
     // Q^T operand: lane (c, g) holds q[row][head][32 s + 8 g .. + 7], s = 0, 1.
     const __bf16 *qrow = q + row * q_stride + int64_t(head) * kHeadDim;
@@ -366,7 +528,6 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
     __syncthreads();
 
     // Thread tid combines query tid / 16, dims 4 (tid % 16) .. + 3.
-    const int cq = tid >> 4, d0 = 4 * (tid & 15);
     float mg[kGroups], M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
@@ -382,53 +543,35 @@ attn2_split(const __bf16 *__restrict__ q, int64_t q_stride, const __bf16 *__rest
         acc += w * *reinterpret_cast<const f32x4 *>(
                        &red[(k * 64 + cq) * kHeadDim + 4 * ((d0 >> 2) ^ (cq & 15))]);
     }
-    const int ct = cq & 7, chh = cq >> 3;      // token and q head of query cq
-    const int64_t crow = int64_t(r) * 8 + ct;
-    const int64_t ccol = int64_t(kQPerKv * j + chh) * kHeadDim + d0;
-    if (Z == 1) {
+    if (geo.nz == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         acc *= inv;
-        float ss = acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3];
-#pragma unroll
-        for (int k = 1; k < 16; k <<= 1)
-            ss += __shfl_xor(ss, k, 64);
+        // The 16 threads of query cq are one DPP row.
+        const float ss =
+            row_sum(acc[0] * acc[0] + acc[1] * acc[1] + acc[2] * acc[2] + acc[3] * acc[3]);
         const float rr = rsqrtf(ss * (1.f / kHeadDim) + kAttn2Eps);
-        const bf16x4 gv = *reinterpret_cast<const bf16x4 *>(gate + crow * gate_stride + ccol);
         bf16x4 res;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             res[v] = __bf16(acc[v] * rr * sigmoidf(float(gv[v])));
         *reinterpret_cast<bf16x4 *>(out + crow * out_stride + ccol) = res;
     } else {
-        // Partial of (request, KV head, split, query cq): max, sum, O[64].
-        float *dst = ws + (((int64_t(r) * nkv + j) * Z + z) * 64 + cq) * kAttn2PartialFloats;
+        // Partial of (split f, KV head, query cq): max, sum, O[64].
+        float *dst = ws + ((int64_t(f) * nkv + j) * 64 + cq) * kAttn2PartialFloats;
         if ((tid & 15) == 0)
             *reinterpret_cast<float2 *>(dst) = make_float2(M, lt);
         *reinterpret_cast<f32x4 *>(dst + 4 + d0) = acc;   // 16-byte aligned
     }
 }
 
-// Merge the non-empty splits of each row in split order, then the norm and
-// the gate.  One wave per output row (request, KV head, row 8 hh + t): lane
-// z reads split z's (max, sum), lane d accumulates dimension d.  All ZMAX
-// loads of a lane are issued before any is used (splits past the last
-// non-empty one read it again with weight 0), so the merge costs one round
-// trip to memory.
+// One output row from its nz splits (nz <= ZMAX, src at split 0, zstride
+// floats between splits): lane z takes split z's (max, sum), lane d sums
+// dimension d over the splits in split order.  All ZMAX loads of a lane are
+// issued before any is used (splits past the last one read it again and
+// weigh 0), so this costs one round trip to memory.
 template <int ZMAX>
-__global__ void __launch_bounds__(256)
-attn2_merge(const __bf16 *__restrict__ gate, int64_t gate_stride, int nkv,
-            const int32_t *__restrict__ seq_lens, int max_len, int window, int Z,
-            const float *__restrict__ ws, __bf16 *__restrict__ out, int64_t out_stride)
+__device__ inline float merge_row(const float *src, int64_t zstride, int nz, int lane)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int id = blockIdx.x * 4 + wave;          // < R * nkv * 64 by the grid
-    const int qr = id & 63, j = (id >> 6) % nkv, r = (id >> 6) / nkv;
-    const int hh = qr >> 3, t = qr & 7;
-    const int L = min(max(seq_lens[r], 8), max_len);
-    const int nz = split_geom(L, window, Z).nz;   // 1 <= nz <= Z <= ZMAX
-    const float *src = ws + ((int64_t(r) * nkv + j) * Z * 64 + qr) * kAttn2PartialFloats;
-    const int64_t zstride = int64_t(64) * kAttn2PartialFloats;
-
     const int zl = min(lane, nz - 1);
     const float2 ml = *reinterpret_cast<const float2 *>(src + zl * zstride);
     float ov[ZMAX];
@@ -442,12 +585,54 @@ attn2_merge(const __bf16 *__restrict__ gate, int64_t gate_stride, int nkv,
     float acc = 0.f;
 #pragma unroll
     for (int zz = 0; zz < ZMAX; ++zz)
-        acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), zz)) * ov[zz];
-    const float o = acc * (lsum > 0.f ? 1.f / lsum : 0.f);
-    const float rr = rsqrtf(wave_sum(o * o) * (1.f / kHeadDim) + kAttn2Eps);
+        acc += lane_f(w, zz) * ov[zz];   // w = 0 past nz
+    return acc * (lsum > 0.f ? 1.f / lsum : 0.f);
+}
+
+// Merge the splits of each row in split order, then the norm and the gate.
+// One wave per output row (request, KV head, row 8 hh + t), which works out
+// the request's splits from the lengths as the split launch did (a request
+// with one split was finished there) and merges them with loads sized to
+// the split count, at most ZCAP.
+template <bool SHARED, int ZCAP>
+__global__ void __launch_bounds__(256)
+attn2_merge(const __bf16 *__restrict__ gate, int64_t gate_stride, int nkv,
+            const int32_t *__restrict__ seq_lens, int R, int max_len, int window, int Z,
+            const float *__restrict__ ws, __bf16 *__restrict__ out, int64_t out_stride)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int id = blockIdx.x * 4 + wave;          // < R * nkv * 64 by the grid
+    const int qr = id & 63, j = (id >> 6) % nkv, r = (id >> 6) / nkv;
+    const int hh = qr >> 3, t = qr & 7;
     const int64_t row = int64_t(r) * 8 + t;
     const int64_t col = int64_t(kQPerKv * j + hh) * kHeadDim + lane;
-    out[row * out_stride + col] = __bf16(o * rr * sigmoidf(float(gate[row * gate_stride + col])));
+    // Fetched first: nothing before the output needs it.
+    const float g = float(gate[row * gate_stride + col]);
+    int off, nz;                                   // 1 <= nz <= ZCAP
+    if constexpr (!SHARED) {
+        nz = split_geom(min(max(seq_lens[r], 8), max_len), window, Z).nz;
+        off = r * Z;
+    } else {
+        const SharedGeom sg = shared_geometry(seq_lens, R, max_len, window, Z, lane);
+        nz = __builtin_amdgcn_readlane(sg.nz, r);
+        off = __builtin_amdgcn_readlane(sg.off, r);
+    }
+    if (nz <= 1)
+        return;   // finished by its split block
+    const int64_t zstride = int64_t(nkv) * 64 * kAttn2PartialFloats;
+    const float *src = ws + ((int64_t(off) * nkv + j) * 64 + qr) * kAttn2PartialFloats;
+    // Loads sized to the request's split count (the same on every lane).
+    float o;
+    if (ZCAP <= 8 || nz <= 8)
+        o = merge_row<8>(src, zstride, nz, lane);
+    else if (ZCAP <= 16 || nz <= 16)
+        o = merge_row<16>(src, zstride, nz, lane);
+    else if (ZCAP <= 32 || nz <= 32)
+        o = merge_row<(ZCAP < 32 ? ZCAP : 32)>(src, zstride, nz, lane);
+    else
+        o = merge_row<ZCAP>(src, zstride, nz, lane);
+    const float rr = rsqrtf(wave_sum(o * o) * (1.f / kHeadDim) + kAttn2Eps);
+    out[row * out_stride + col] = __bf16(o * rr * sigmoidf(g));
 }
 
 }  // namespace
@@ -455,27 +640,32 @@ attn2_merge(const __bf16 *__restrict__ gate, int64_t gate_stride, int nkv,
 hipError_t launch_attn2(const void *q, int64_t q_stride, const void *gate, int64_t gate_stride,
                         const void *kv_cache, int nkv, const int32_t *block_table,
                         int64_t bt_stride, const int32_t *seq_lens, int R, int max_len,
-                        int window, int Z, float *ws, void *out, int64_t out_stride,
-                        hipStream_t stream)
+                        int window, const Attn2Launch &l, float *ws, void *out,
+                        int64_t out_stride, hipStream_t stream)
 {
-    hipLaunchKernelGGL(attn2_split, dim3(Z, nkv, R), dim3(kThreads), 0, stream,
-                       static_cast<const __bf16 *>(q), q_stride, static_cast<const __bf16 *>(gate),
-                       gate_stride, static_cast<const __bf16 *>(kv_cache), nkv, block_table,
-                       bt_stride, seq_lens, max_len, window, Z, ws, static_cast<__bf16 *>(out),
+    // Shared slots must exceed the request count (every request has a split
+    // and the split search ends); a merge needs the workspace.
+    if ((l.shared && l.slots <= R) || l.zmax > kAttn2MaxSplits || (l.zmax > 1 && ws == nullptr))
+        return hipErrorInvalidValue;
+    const dim3 grid(l.slots, nkv, l.shared ? 1 : R);
+    auto split = l.shared ? attn2_split<true> : attn2_split<false>;
+    hipLaunchKernelGGL(split, grid, dim3(kThreads), 0, stream, static_cast<const __bf16 *>(q),
+                       q_stride, static_cast<const __bf16 *>(gate), gate_stride,
+                       static_cast<const __bf16 *>(kv_cache), nkv, block_table, bt_stride,
+                       seq_lens, R, max_len, window, l.slots, ws, static_cast<__bf16 *>(out),
                        out_stride);
-    if (Z > 1) {
-        const dim3 grid(R * nkv * 64 / 4);
+    if (l.zmax > 1) {
+        const dim3 mgrid(R * nkv * 64 / 4);
         auto *gp = static_cast<const __bf16 *>(gate);
         auto *op = static_cast<__bf16 *>(out);
-        if (Z <= 16)
-            hipLaunchKernelGGL(attn2_merge<16>, grid, dim3(256), 0, stream, gp, gate_stride, nkv,
-                               seq_lens, max_len, window, Z, ws, op, out_stride);
-        else if (Z <= 32)
-            hipLaunchKernelGGL(attn2_merge<32>, grid, dim3(256), 0, stream, gp, gate_stride, nkv,
-                               seq_lens, max_len, window, Z, ws, op, out_stride);
-        else
-            hipLaunchKernelGGL(attn2_merge<64>, grid, dim3(256), 0, stream, gp, gate_stride, nkv,
-                               seq_lens, max_len, window, Z, ws, op, out_stride);
+        auto merge = l.shared ? (l.zmax <= 16   ? attn2_merge<true, 16>
+                                 : l.zmax <= 32 ? attn2_merge<true, 32>
+                                                : attn2_merge<true, 64>)
+                              : (l.zmax <= 16   ? attn2_merge<false, 16>
+                                 : l.zmax <= 32 ? attn2_merge<false, 32>
+                                                : attn2_merge<false, 64>);
+        hipLaunchKernelGGL(merge, mgrid, dim3(256), 0, stream, gp, gate_stride, nkv, seq_lens, R,
+                           max_len, window, l.slots, ws, op, out_stride);
     }
     return hipGetLastError();
 }

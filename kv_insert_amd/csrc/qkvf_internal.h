@@ -101,18 +101,21 @@ constexpr int attn2_q_piece(int g, int h) { return 32 * h + 8 * g; }
 static_assert(attn2_q_piece(3, 1) + 8 <= kHeadDim && attn2_q_piece(0, 0) >= 0,
               "q pieces lie inside the head");
 
-// Key splits of an attn2 launch.  A request's rows span at most
-// max_model_len keys (window + 7 with a window); the keys are cut into about
-// kAttn2TargetBlocks / (num_reqs * nkv) splits so that a launch has ~256
-// blocks (one 16-wave block per CU), but no split is shorter than
-// kAttn2MinSplitKeys keys (each split writes a 17 KB partial per KV head) and
-// there are at most 64.
-// The count depends on the deployment and the batch size, not on the step's
-// lengths, so the launch shape is fixed for a captured batch size; shorter
-// contexts leave the trailing splits empty.  A layer prepared with
-// batch-invariant splits uses the one-request count for every batch size, so
-// a request's output bits do not depend on the other requests of its batch
-// (at the price of more blocks and partials for larger batches).
+// Key splits of an attn2 launch.  A launch aims at ~kAttn2TargetBlocks
+// blocks (one 16-wave block per CU): ceil(kAttn2TargetBlocks / nkv) split
+// slots per KV head.  No split is shorter than kAttn2MinSplitKeys keys (each
+// split writes a 17 KB partial per KV head), so a request spans at most one
+// split per kAttn2MinSplitKeys keys of the span its rows attend
+// (max_model_len, or window + 7), and at most kAttn2MaxSplits.
+// One request takes min(slots, its span's splits).  Several requests share
+// the slots: one split length for the whole launch, the shortest (in whole
+// key steps) for which all requests' splits fit, so a long request gets more
+// splits than a short one and the blocks finish together.  The slot count
+// depends on the deployment and the batch size only, so the launch shape of
+// a batch size is fixed; shorter contexts leave trailing slots empty.  A
+// layer prepared with batch-invariant splits gives every request the
+// one-request split count (grid: splits x KV heads x requests), so a
+// request's output bits do not depend on the other requests of its batch.
 constexpr int kAttn2TargetBlocks = 256;
 constexpr int kAttn2MinSplitKeys = 128;
 constexpr int kAttn2MaxSplits = 64;
@@ -122,41 +125,75 @@ inline int attn2_span(int max_model_len, int window)
     return window > 0 && window + 7 < max_model_len ? window + 7 : max_model_len;
 }
 
+// Split slots per KV head for num_reqs requests sharing them; 1 when no
+// request can take more than one split (no merge pass).  With num_reqs = 1
+// it is the split count of one request.
 inline int attn2_splits(int nkv, int num_reqs, int max_model_len, int window)
 {
     const int span = attn2_span(max_model_len, window);
-    const int by_len = (span + kAttn2MinSplitKeys - 1) / kAttn2MinSplitKeys;
-    const int per_req = nkv * num_reqs;
-    int z = (kAttn2TargetBlocks + per_req - 1) / per_req;
-    if (z > by_len)
-        z = by_len;
-    if (z > kAttn2MaxSplits)
-        z = kAttn2MaxSplits;
-    return z < 2 ? 1 : z;
+    int by_len = (span + kAttn2MinSplitKeys - 1) / kAttn2MinSplitKeys;
+    if (by_len > kAttn2MaxSplits)
+        by_len = kAttn2MaxSplits;
+    const int per_head = (kAttn2TargetBlocks + nkv - 1) / nkv;
+    const int64_t most = int64_t(num_reqs) * by_len;
+    const int b = most < per_head ? int(most) : per_head;
+    return b > num_reqs ? b : 1;
 }
 
-// Workspace floats for every batch size up to max_reqs (with batch-invariant
-// splits every batch uses the one-request split count).
+// The launch shape of a call: `slots` split blocks per KV head along grid x,
+// per request (shared == false: grid slots x nkv x num_reqs) or shared by the
+// requests (grid slots x nkv); zmax bounds one request's split count (1: no
+// merge pass).  Shared slots always exceed num_reqs.
+struct Attn2Launch {
+    int slots;
+    bool shared;
+    int zmax;
+};
+
+inline Attn2Launch attn2_launch(int nkv, int num_reqs, int max_model_len, int window,
+                                bool invariant)
+{
+    if (invariant || num_reqs == 1) {
+        const int z = attn2_splits(nkv, 1, max_model_len, window);
+        return Attn2Launch{z, false, z};
+    }
+    const int b = attn2_splits(nkv, num_reqs, max_model_len, window);
+    if (b == 1)
+        return Attn2Launch{1, false, 1};
+    const int zmax = b - (num_reqs - 1);
+    return Attn2Launch{b, true, zmax < kAttn2MaxSplits ? zmax : kAttn2MaxSplits};
+}
+
+// Workspace floats of a call (0: no merge pass, no workspace).
+inline size_t attn2_call_floats(const Attn2Launch &l, int nkv, int num_reqs)
+{
+    if (l.zmax <= 1)
+        return 0;
+    const size_t blocks = size_t(l.shared ? 1 : num_reqs) * l.slots * nkv;
+    return blocks * 64 * kAttn2PartialFloats;
+}
+
+// Workspace floats for every batch size up to max_reqs.
 inline size_t attn2_workspace_floats(int nkv, int max_reqs, int max_model_len, int window,
                                      bool invariant = false)
 {
     size_t most = 0;
     for (int r = 1; r <= max_reqs; ++r) {
-        const int z = attn2_splits(nkv, invariant ? 1 : r, max_model_len, window);
-        const size_t n = z > 1 ? size_t(r) * nkv * z * 64 * kAttn2PartialFloats : 0;
+        const size_t n =
+            attn2_call_floats(attn2_launch(nkv, r, max_model_len, window, invariant), nkv, r);
         if (n > most)
             most = n;
     }
     return most;
 }
 
-// Enqueue attn2 (and its merge when Z > 1) on `stream`; arguments validated
-// by the caller; ws holds R * nkv * Z * 64 * kAttn2PartialFloats floats.
+// Enqueue attn2 (and its merge when l.zmax > 1) on `stream`; arguments
+// validated by the caller; ws holds attn2_call_floats(l, nkv, R) floats.
 hipError_t launch_attn2(const void *q, int64_t q_stride, const void *gate, int64_t gate_stride,
                         const void *kv_cache, int nkv, const int32_t *block_table,
                         int64_t bt_stride, const int32_t *seq_lens, int R, int max_len,
-                        int window, int Z, float *ws, void *out, int64_t out_stride,
-                        hipStream_t stream);
+                        int window, const Attn2Launch &l, float *ws, void *out,
+                        int64_t out_stride, hipStream_t stream);
 
 // LayerFront: rows of kHidden values, one block per row.
 constexpr int64_t kLayerFrontMaxRows = int64_t(1) << 20;

@@ -31,8 +31,8 @@ hipError_t launch_stream_read(const void *, size_t, unsigned *, hipStream_t)
 }
 
 hipError_t launch_attn2(const void *, int64_t, const void *, int64_t, const void *, int,
-                        const int32_t *, int64_t, const int32_t *, int, int, int, int, float *,
-                        void *, int64_t, hipStream_t)
+                        const int32_t *, int64_t, const int32_t *, int, int, int,
+                        const Attn2Launch &, float *, void *, int64_t, hipStream_t)
 {
     ++g_stub_launches;
     return hipErrorInvalidValue;

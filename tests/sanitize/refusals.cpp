@@ -113,7 +113,7 @@ int main()
                 for (int reqs : {1, 2, 3, 40, 64}) {
                     int z = -1;
                     const int st = qkvf_attn2_plan(nkv, len, window, reqs, &z);
-                    if (st != 0 || z < 1 || z > 64)
+                    if (st != 0 || z < 1 || z > 256 || (z > 1 && z <= reqs) || (reqs == 1 && z > 64))
                         expect("attn2 plan", st * 100 + z, 0);
                 }
     expect("attn2 plan reqs", qkvf_attn2_plan(8, 4096, 0, 0, nullptr), 3);

@@ -118,6 +118,12 @@ SWEEP = [
     (8, 16384, 7, (8, 15, 16, 300)),
     (2, 16384, 8, (16, 17, 1000)),
     (2, 2048, 4096, (8, 500, 2048)),      # window covering every position: none
+    # requests sharing the split slots: equal lengths whose first split length
+    # does not fit (a bisection), and mixed lengths where short requests take
+    # one split (finished by their block) beside long ones (merged)
+    (8, 4096, 0, (1600,) * 12),
+    (4, 65536, 0, (60000, 8, 100, 3000)),
+    (2, 131072, 2000, (131072, 9, 2500, 40000)),
 ]
 
 

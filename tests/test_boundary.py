@@ -158,16 +158,19 @@ def test_no_device_here_means_device_error(L):
 
 
 @pytest.mark.parametrize("nkv,mml,window,reqs,splits", [
-    (8, 131072, 0, 1, 32), (8, 32768, 0, 2, 16), (1, 131072, 0, 1, 64), (2, 4096, 0, 1, 32),
-    (4, 8192, 0, 3, 22), (8, 2048, 0, 1, 16), (8, 128, 0, 1, 1), (8, 129, 0, 1, 2),
-    (8, 256, 0, 1, 2), (8, 257, 0, 1, 3), (8, 131072, 4096, 2, 16), (8, 131072, 4096, 1, 32),
+    (8, 131072, 0, 1, 32), (8, 32768, 0, 2, 32), (1, 131072, 0, 1, 64), (2, 4096, 0, 1, 32),
+    (4, 8192, 0, 3, 64), (8, 2048, 0, 1, 16), (8, 128, 0, 1, 1), (8, 129, 0, 1, 2),
+    (8, 256, 0, 1, 2), (8, 257, 0, 1, 3), (8, 131072, 4096, 2, 32), (8, 131072, 4096, 1, 32),
     (8, 131072, 8192, 1, 32), (2, 2048, 4096, 1, 16),
-    (1, 8, 0, 1, 1), (8, 131072, 0, 64, 1), (8, 131072, 0, 40, 1), (1, 2048, 1, 1, 1),
-    (2, 131072, 0, 40, 4),
+    (1, 8, 0, 1, 1), (8, 131072, 0, 64, 1), (8, 131072, 0, 40, 1), (8, 131072, 0, 31, 32),
+    (1, 2048, 1, 1, 1), (2, 131072, 0, 40, 128), (1, 131072, 0, 64, 256), (1, 256, 0, 64, 128),
+    (4, 256, 0, 2, 4), (4, 128, 0, 2, 1), (8, 4096, 0, 32, 1),
 ])
 def test_attn2_plan(L, nkv, mml, window, reqs, splits):
-    """Split count: ceil(256 / (reqs nkv)) capped by one split per 128 keys of
-    the span (max_model_len, or window + 7) and by 64; 1 below 2."""
+    """Split slots per KV head: ceil(256 / nkv), capped by reqs x the splits
+    one request can take (one per 128 keys of the span, max_model_len or
+    window + 7, and at most 64); 1 when that is not more than reqs (every
+    request one split, no merge)."""
     import ctypes
     z = ctypes.c_int(-1)
     assert L.qkvf_attn2_plan(nkv, mml, window, reqs, ctypes.byref(z)) == 0
