@@ -93,6 +93,9 @@ def parse():
                     help="instead of timing, issue warmup + steps front calls of each workload "
                          "in turn on one stream (for a rocprofv3 run); one JSON line per "
                          "workload on stdout names its calls, in order")
+    ap.add_argument("--summarize-attn2-profiles", default="", metavar="DIR",
+                    help="summarize attn2 kernel traces and counters under DIR/a2/<workload>/ "
+                         "into profiles/attn2_counters.json and print a table")
     ap.add_argument("--summarize-profiles", default="", metavar="DIR",
                     help="no GPU: read the rocprofv3 output of a --profile-workloads run under "
                          "DIR (order.jsonl, trace/, fetch/, write/, calib_fetch/, calib_write/, "
@@ -712,6 +715,97 @@ def summarize_profiles(d: str, out: str | None = None) -> str:
     return table
 
 
+def summarize_attn2_profiles(d: str, out: str | None = None) -> str:
+    """attn2 summary from a profiling directory: per workload W, the kernel
+    trace under a2/W/trace and, where taken, FETCH_SIZE / WRITE_SIZE under
+    a2/W/fetch and a2/W/write (each a `bench.py --attn2 W` run); the copy
+    calibration and the --all event lines (all.jsonl) of the front's run in
+    the same directory.  The first `skip` dispatches of each kernel are the
+    run's warm-up."""
+    import statistics
+    skip = 20
+    calib = json.load(open(os.path.join(d, "calibration.json")))
+
+    def copy_median(sub: str, counter: str) -> float:
+        return statistics.median(float(r["Counter_Value"]) for r in
+                                 _csv_rows(os.path.join(d, sub), "counter_collection.csv")
+                                 if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter)
+
+    fetch_factor = calib["copy_bytes_read"] / (copy_median("calib_fetch", "FETCH_SIZE") * 1024)
+    write_factor = calib["copy_bytes_written"] / (copy_median("calib_write", "WRITE_SIZE") * 1024)
+    events = {}
+    all_path = os.path.join(d, "all.jsonl")
+    if os.path.exists(all_path):
+        for l in open(all_path):
+            if l.startswith("{") and '"workload"' in l:
+                rec = json.loads(l)
+                events[rec["workload"]] = rec
+    record = {"kernel_source": os.path.relpath(ATTN2_SRC, ROOT),
+              "kernel_sha256_16": kernel_hash(ATTN2_SRC),
+              "fetch_scale": round(fetch_factor, 5), "write_scale": round(write_factor, 5),
+              "calibration": "device-to-device copy of "
+                             f"{calib['copy_bytes_read'] / 1e6:.0f} MB (torch copy_)",
+              "workloads": {}}
+    lines = ["| Workload | splits | bench.py us/call | trace attn2_split avg (min / max) us | "
+             "trace attn2_merge avg (min / max) us | algorithmic bytes | GB/s | frac of 8 TB/s | "
+             "HBM bytes per call (counters, scaled) | traffic / algorithmic | "
+             "oracle us/call (threads / host cores) |", "|" + "---|" * 11]
+
+    def stats(rows):
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows][skip:]
+        return (sum(dur) / len(dur), min(dur), max(dur), len(dur)) if dur else None
+
+    for name in sorted(os.listdir(os.path.join(d, "a2")),
+                       key=lambda n: list(wl.ATTN2_WORKLOADS).index(n)):
+        w = wl.ATTN2_WORKLOADS[name]
+        base = os.path.join(d, "a2", name)
+        tr = _csv_rows(os.path.join(base, "trace"), "kernel_trace.csv")
+        sp = stats(sorted((r for r in tr if "attn2_split" in r["Kernel_Name"]),
+                          key=lambda r: int(r["Dispatch_Id"])))
+        mg = stats(sorted((r for r in tr if "attn2_merge" in r["Kernel_Name"]),
+                          key=lambda r: int(r["Dispatch_Id"])))
+        entry = {"trace_split_avg_us": round(sp[0], 3), "trace_split_min_us": round(sp[1], 3),
+                 "trace_split_max_us": round(sp[2], 3), "trace_dispatches": sp[3]}
+        if mg:
+            entry.update(trace_merge_avg_us=round(mg[0], 3), trace_merge_min_us=round(mg[1], 3),
+                         trace_merge_max_us=round(mg[2], 3))
+        hbm = None
+        if os.path.isdir(os.path.join(base, "fetch")):
+            kib = {}
+            for sub, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+                rows = _csv_rows(os.path.join(base, sub), "counter_collection.csv")
+                for kern in ("split", "merge"):
+                    v = [float(r["Counter_Value"]) for r in rows
+                         if f"attn2_{kern}" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+                    kib[f"{kern}_{sub}_kib"] = statistics.median(v) if v else 0.0
+            hbm = ((kib["split_fetch_kib"] + kib["merge_fetch_kib"]) * fetch_factor +
+                   (kib["split_write_kib"] + kib["merge_write_kib"]) * write_factor) * 1024
+            entry.update(kib, hbm_bytes_per_call=int(round(hbm)))
+        record["workloads"][name] = entry
+        alg = w.algorithmic_bytes()
+        ev = events.get(name, {})
+        us = ev.get("us_per_call")
+        gbs = alg / (us * 1e-6) / 1e9 if us else None
+        cb = ev.get("cpu_baseline") or {}
+        cell = lambda v, f: "n/a" if v is None else f.format(v)
+        merge_cell = f"{mg[0]:.2f} ({mg[1]:.2f} / {mg[2]:.2f})" if mg else "-"
+        lines.append(
+            f"| {name} | {qf.attn2_plan(w.nkv, w.max_model_len, w.window, w.R)} | "
+            f"{cell(us, '{:.2f}')} | {sp[0]:.2f} ({sp[1]:.2f} / {sp[2]:.2f}) | {merge_cell} | "
+            f"{alg:,} | {cell(gbs, '{:.0f}')} | {cell(gbs and gbs / HBM_PEAK_GBS, '{:.3f}')} | "
+            f"{cell(hbm, '{:,.0f}')} | {cell(hbm and hbm / alg, '{:.3f}')} | "
+            f"{cell(cb.get('us_per_call'), '{:,.0f}')} ({cb.get('cores', '-')} / "
+            f"{cb.get('host_cores', '-')}) |")
+    out = out or ATTN2_COUNTERS
+    with open(out, "w") as fh:
+        json.dump(record, fh, indent=1)
+        fh.write("\n")
+    table = "\n".join(lines)
+    print(table)
+    print(f"\nwrote {out}", file=sys.stderr)
+    return table
+
+
 def all_lines(a) -> None:
     """One JSON line per workload and sweep point on stderr: timing, the
     roofline with counter traffic when recorded for this kernel source, and
@@ -768,6 +862,9 @@ def main():
     a = parse()
     if a.summarize_profiles:
         summarize_profiles(a.summarize_profiles)
+        return
+    if a.summarize_attn2_profiles:
+        summarize_attn2_profiles(a.summarize_attn2_profiles)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on exactly one GPU (asked for {a.gpus}); the front is a "
