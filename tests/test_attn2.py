@@ -293,19 +293,29 @@ def test_attn2_refusals_on_device():
     assert bool((out.view(torch.int16) == CANARY).all())
 
 
-def test_attn2_graph_replays():
+GRAPH_CASES = [
+    # (first lengths, the lengths of the three replays)
+    ((9000,), [(9000,), (8000,), (7000,)]),
+    # requests sharing the split slots: each replay's lengths give another
+    # split length and another share of the slots, from the same launch
+    ((20000, 9000, 300), [(20000, 9000, 300), (300, 8, 20000), (12000, 12000, 12000)]),
+]
+
+
+@pytest.mark.parametrize("first,replays", GRAPH_CASES, ids=["one_request", "shared_slots"])
+def test_attn2_graph_replays(first, replays):
     """Captured once, replayed with new inputs copied into the captured
     buffers (eager work between replays); every replay matches eager."""
-    a = wl.Attn2Workload("graph", nkv=8, max_model_len=65536, lens=(9000,), index=34)
+    a = wl.Attn2Workload("graph", nkv=8, max_model_len=65536, lens=first, index=34)
     case = Attn2Case(a)
     dev = "cuda"
     y = case.y.cuda()
     q, g = wl.attn2_views(y, a.nkv)
     cache, table, lens = case.cache.cuda(), case.table.cuda(), case.lens.cuda()
-    out = new_out(8, 8 * a.nkv * 64)
+    out = new_out(8 * a.R, 8 * a.nkv * 64)
     case.host_check()
-    say("attn2 graph capture")
-    qf.attn2_prepare(a.nkv, a.max_model_len, 1, 0)
+    say(f"attn2 graph capture R={a.R}")
+    qf.attn2_prepare(a.nkv, a.max_model_len, a.R, 0)
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
@@ -314,10 +324,13 @@ def test_attn2_graph_replays():
         stream.synchronize()
         with torch.cuda.graph(graph, stream=stream):
             qf.attn2_run(q, g, cache, table, lens, out, stream=stream)
-    for i in range(3):
+    for i, new_lens in enumerate(replays):
         ys = wl.make_attn2_y(a, set_index=1 + i)
         y.copy_(ys.to(dev))
-        lens.fill_(9000 - 1000 * i)
+        # within the pages each request owns (the table's other entries are
+        # the filler page)
+        assert all(L <= max(first) for L in new_lens)
+        lens.copy_(torch.tensor(new_lens, dtype=torch.int32))
         torch.cuda.synchronize()
         say(f"attn2 graph replay {i}")
         graph.replay()
