@@ -11,11 +11,13 @@
 //    into S K ranges (S = 4 for 8 KV heads, else 8) and row groups: block b
 //    owns one K range of 8192/S and 2 to 9 row tiles of 16 W rows, so every
 //    partial it produces is read on its own XCD.  For each tile the block
-//      - loads the 16 rows with non-temporal 16-byte loads, each wave
-//        instruction reading 1 KB of one row (the shape HBM streams best),
-//        several tiles ahead of use, into registers;
-//      - stores them into an LDS tile whose 16-byte chunks are XOR-swizzled
-//        by row, so the transposed reads below hit distinct banks;
+//      - loads the 16 rows with non-temporal 16-byte loads straight into
+//        LDS (buffer loads with the lds bit), each wave instruction reading
+//        1 KB of one row (the shape HBM streams best), into a ring of 2 or 3
+//        tile buffers, so the next tiles stream while one is used; the
+//        16-byte chunks land XOR-swizzled by row (each lane fetches the chunk
+//        its LDS position needs), so the transposed reads below hit
+//        distinct banks;
 //      - reads the tile back in MFMA operand layout, each wave its own 1/8 of
 //        the block's K range, and issues v_mfma_f32_16x16x32_bf16 with W as
 //        the 16-row A operand and the tokens (x, held in registers for the
@@ -34,8 +36,9 @@
 //    and of the token's K|V slot.
 //
 //  No read-modify-write atomics, no flags, no counters and no cache
-//  maintenance; every hand-off stays inside one XCD's L2.  Between calls every partial word holds kPartialEmpty (a NaN
-//  pattern no partial takes: a partial with those bits is stored as the
+//  maintenance; every hand-off stays inside one XCD's L2.  Between calls
+//  every partial word holds kPartialEmpty (a NaN pattern no partial takes:
+//  a partial with those bits is stored as the
 //  canonical NaN), so a word that is not empty holds this call's partial:
 //  each word has one producer and one reader per call, and the reader
 //  empties it after use, so every call leaves the workspace as it found it.
@@ -91,12 +94,14 @@ struct Shape {
     static constexpr int CHUNKS = KB / 8;          // 16-byte chunks per tile row
     static constexpr int LOADS = 2 * CHUNKS / 64;  // 1 KB loads per wave per tile (2 rows)
     static constexpr int TILE_BYTES = kTileRows * KB * 2;
-    static constexpr int LDS_BYTES = 2 * TILE_BYTES;
+    // Tiles in the LDS ring: measured on one box against rings of 2, 3 and
+    // 4 tiles (C1 6.87 / 7.03 / 7.12 us, C2 9.13 at 2 or 3 against 10.04 at
+    // 4, nkv = 4 at M = 1 14.35 / 14.10 / 14.36 us); 64 KB tiles allow 2.
+    static constexpr int NB = NKV == 1 || NKV == 8 ? 2 : 3;
     // XCD x owns heads [x HEADS / 8, (x + 1) HEADS / 8); its 32 blocks take
     // the S splits of 32 / S row groups of those heads' tiles.
     static constexpr int MAX_HEADS = (HEADS + 7) / 8;
     static constexpr int U_MAX = MAX_HEADS * 4 * S / 32;   // tiles per block, at most
-    static constexpr int DEPTH = (12 / LOADS) < U_MAX ? (12 / LOADS) : U_MAX;
     static_assert(KW % 32 == 0 && CHUNKS % 16 == 0, "whole MFMA steps, whole swizzle groups");
     static_assert(LOADS * 64 == 2 * CHUNKS, "each wave loads exactly two tile rows");
     static_assert((HEADS / 8) * 4 * S % 32 == 0 && MAX_HEADS * 4 * S % 32 == 0, "whole tiles per block");
@@ -107,14 +112,10 @@ __device__ inline bf16x8 load16(const __bf16 *p)
     return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-// W is read once: non-temporal loads keep it from displacing reused lines.
-// They go through a buffer descriptor over W with 32-bit byte offsets, which
-// measured faster than global loads of 64-bit addresses with the same policy.
-__device__ inline bf16x8 stream16(__amdgpu_buffer_rsrc_t w, int off)
-{
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(w, off, 0, kCacheNt);
-    return __builtin_bit_cast(bf16x8, v);
-}
+// W is read once: its loads are non-temporal, which keeps it from displacing
+// reused lines.  They go through a buffer descriptor over W with 32-bit byte
+// offsets, which measured faster than global loads of 64-bit addresses with
+// the same policy.
 
 // A lane's value moved by a DPP control code within its row of 16 lanes.
 template <int CTRL>
@@ -154,10 +155,29 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             unsigned spin_limit)
 {
     using Sh = Shape<NKV>;
-    constexpr int ST = Sh::STEPS, D = Sh::DEPTH, U = Sh::U_MAX, C = Sh::CHUNKS;
+    constexpr int ST = Sh::STEPS, U = Sh::U_MAX, C = Sh::CHUNKS;
     constexpr int LD = Sh::LOADS, N = Sh::N, NQ = kQPerKv * NKV;
     constexpr size_t kTileStride = size_t(kTileRows) * kHidden;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[Sh::LDS_BYTES];
+    // The LDS ring, one array per buffer: the compiler then sees that a
+    // load into one buffer cannot alias reads of another, and waits only for
+    // the loads into the buffer it reads.
+    __shared__ __attribute__((aligned(16))) unsigned char lds0[Sh::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char lds1[Sh::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char lds2[Sh::NB > 2 ? Sh::TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char lds3[Sh::NB > 3 ? Sh::TILE_BYTES : 16];
+    auto bufp = [&](int i) -> unsigned char * {
+        return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : lds3;
+    };
+    // A block barrier without a memory fence (a fence would wait for every
+    // load into LDS in flight): LDS stores of this wave done, then s_barrier;
+    // the empty asm statements keep the compiler from moving memory accesses
+    // across it.
+    auto block_barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt unconstrained
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
 
     unsigned *parts = ws;
     const int b = blockIdx.x;
@@ -207,8 +227,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // Token columns r >= M repeat row M-1; their MFMA outputs are never used.
     // x comes from L2 and is first needed at tile 0's MFMAs.  Loading it
     // behind the weight prologue lets the stream start earlier (measured
-    // faster for NKV >= 2); with NKV = 1 every tile is requested up front
-    // and x goes first (measured faster there).
+    // faster for every NKV: C1 6.92 -> 6.80 us, C3 0.12-0.26 us).
     const int xrow = r < M ? r : M - 1;
     bf16x8 xv[ST];
     auto load_x = [&]() {
@@ -216,39 +235,49 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         for (int st = 0; st < ST; ++st)
             xv[st] = load16(x + size_t(xrow) * kHidden + k0 + chunk_of(st) * 8);
     };
-    if constexpr (NKV == 1)
-        load_x();
 
-    // Load j of this wave covers chunk c of tile row `row` (rows 2w, 2w+1);
-    // it lands in LDS chunk row * C + (c ^ row).
     // Byte offsets into W, which is at most 9216 x 8192 bf16 (151 MB).
     static_assert(size_t(N) * kHidden * 2 < (size_t(1) << 31), "W offsets fit 31 bits");
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(W), 0, int(size_t(N) * kHidden * 2), kBufferConfig);
     const int wtile = int((size_t(tile0 * kTileRows) * kHidden + k0) * 2);
     constexpr int kTileBytes = int(kTileStride * 2);
-    int goff[LD];
-    int loff[LD];
+    // Tile t goes straight into LDS ring buffer t % NB.  Load j of a wave
+    // covers 64 consecutive chunks c0 .. c0 + 63 of tile row `row` (rows 2w,
+    // 2w + 1), which land, swizzled, in LDS chunks row * C + c0 + (c ^ row):
+    // the 64 lanes write 1 KB of LDS in lane order, so lane l fetches the
+    // chunk that belongs at c0 + l, global chunk c0 + (l ^ row) (the same
+    // 1 KB of W in another lane order).
+    auto issue = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < LD; ++j) {
-        const int L = j * 64 + lane;
-        const int row = 2 * wave + L / C;
-        const int c = L % C;
-        goff[j] = (row * kHidden + c * 8) * 2;
-        loff[j] = (row * C + (c ^ (row & 15))) * 16;
-    }
-
-    bf16x8 ring[D][LD];
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-        if (u < ub) {
-#pragma unroll
-            for (int j = 0; j < LD; ++j)
-                ring[u][j] = stream16(wr, wtile + u * kTileBytes + goff[j]);
+        for (int j = 0; j < LD; ++j) {
+            const int row = 2 * wave + (j * 64) / C;
+            const int c0 = (j * 64) % C;
+            const int loff = (row * C + c0) * 16;
+            const int goff = (row * kHidden + (c0 + (lane ^ (row & 15))) * 8) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (__attribute__((address_space(3))) void *)(bufp(t % Sh::NB) + loff), 16,
+                wtile + t * kTileBytes + goff, 0, 0, kCacheNt);
         }
-    }
-    if constexpr (NKV != 1)
-        load_x();
+    };
+    // Wait until at most `later` tiles of this wave's loads are in flight
+    // (s_waitcnt takes an immediate; loads and stores count in issue order,
+    // so anything issued after those tiles only makes the wait longer).
+    auto wait_tiles = [&](int later) {
+        auto imm = [](int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70 | 0xF00; };
+        switch (later) {
+        case 0: __builtin_amdgcn_s_waitcnt(imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(imm(LD)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(imm(2 * LD < 63 ? 2 * LD : 63)); break;
+        default: __builtin_amdgcn_s_waitcnt(imm(3 * LD < 63 ? 3 * LD : 63)); break;
+        }
+    };
+    static_assert(Sh::NB <= 4 && 3 * LD <= 63, "wait counts");
+#pragma unroll
+    for (int t = 0; t < Sh::NB - 1; ++t)
+        if (t < ub)
+            issue(t);
+    load_x();
 
     // The token's rotation for this lane's pair and the fault word, fetched
     // while W streams.  The barriers keep these loads behind the weight
@@ -258,7 +287,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     const float *cs_row = cos_sin != nullptr ? cos_sin + pos_t * kHeadDim
                                              : reinterpret_cast<const float *>(ws);
     float rc = cs_row[pi], rs = cs_row[32 + pi];
-    const unsigned fault_in =
+    const unsigned fault_v =
         __hip_atomic_load(ws + kFaultWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -285,35 +314,39 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     };
     constexpr int SLAB = kWaves * kTileRows * (kTileRows + 1);  // floats per tile
 
-    // Large tiles (NKV >= 4) reduce each tile inside the loop, where LDS has
-    // spare bandwidth: the 8 wave partials of tile u go to red[u & 1] right
-    // after its MFMAs and, one barrier later (all waves have written them),
-    // are summed and stored while tile u + 1 streams; red[u & 1] is written
-    // again only after the barrier that follows the sum.  (Keeping the sums
-    // in registers and storing all 9 after the stream measured slower: 25.3
-    // against 24.9 us at M = 8, 26.8 against 26.1 us at M = 16.)  Small
-    // tiles keep the loop short and reduce all tiles after it.  Lane (r, q)
-    // holds D[row = 4q + v][token = r], v = 0..3; token columns r >= M are
-    // never needed.
+    // Each tile is reduced inside the loop, where LDS has spare bandwidth:
+    // the 8 wave partials of tile u go to red[u & 1] right after its MFMAs
+    // and, one barrier later (all waves have written them), are summed and
+    // stored while later tiles stream; red[u & 1] is written again only
+    // after the barriers that follow the sum.  (Keeping the sums in registers
+    // and storing all 9 after the stream measured slower: 25.3 against
+    // 24.9 us at M = 8, 26.8 against 26.1 us at M = 16.)  Lane (r, q) holds
+    // D[row = 4q + v][token = r], v = 0..3; token columns r >= M are never
+    // needed.
+    //
+    // Per tile u: a barrier frees the buffer of tile u - 1, tile u + NB - 1
+    // is sent into it, the sum of tile u - 1 is stored, and after this
+    // wave's loads of tile u have landed a second barrier waits for every
+    // wave's; then the MFMAs read tile u from LDS.
     __shared__ float red[2][SLAB];
     const bool summer = threadIdx.x < kTileRows * M;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (u >= ub)
             break;
-        unsigned char *tile = lds + (u & 1) * Sh::TILE_BYTES;
-#pragma unroll
-        for (int j = 0; j < LD; ++j)
-            *reinterpret_cast<bf16x8 *>(tile + loff[j]) = ring[u % D][j];
-        if (u + D < ub) {
-#pragma unroll
-            for (int j = 0; j < LD; ++j)
-                ring[u % D][j] = stream16(wr, wtile + (u + D) * kTileBytes + goff[j]);
-        }
-        __syncthreads();
+        // Every wave is done with tile u - 1 (its buffer is free again) and
+        // has written its partials of it to red[(u - 1) & 1].
+        if (u > 0)
+            block_barrier();
+        if (u + Sh::NB - 1 < ub)
+            issue(u + Sh::NB - 1);
         if (u > 0 && summer)
             store_partial(block_sum(red[(u - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
                           u - 1, threadIdx.x >> 4, threadIdx.x & 15);
+        // This wave's loads of tile u have landed, then everyone's have.
+        wait_tiles(min(u + Sh::NB - 1, ub - 1) - u);
+        block_barrier();
+        const unsigned char *tile = bufp(u % Sh::NB);
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < ST; ++st) {
@@ -335,6 +368,11 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // A device left in the fault state by an earlier call: no reader runs,
     // so no y or cache entry is stored (partials stored above are emptied
     // when the host clears the fault).
+    // The word is read here through an opaque copy: a branch on the loaded
+    // value itself would make the compiler wait for it (and for every load
+    // issued before it) ahead of the loop.
+    unsigned fault_in;
+    asm volatile("" : "=v"(fault_in) : "0"(fault_v));
     if (fault_in != 0)
         return;
 
