@@ -146,7 +146,8 @@ __device__ inline unsigned pack2(__bf16 lo, __bf16 hi)
            (unsigned(__builtin_bit_cast(unsigned short, hi)) << 16);
 }
 
-template <int NKV>
+// XFIRST: x is loaded ahead of the weight prologue (chosen at launch).
+template <int NKV, bool XFIRST>
 __global__ void __launch_bounds__(kWaves * 64, 1)
 front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const int64_t *__restrict__ positions, const int64_t *__restrict__ slots,
@@ -225,9 +226,8 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     auto chunk_of = [&](int st) { return wave * 4 * ST + st * 4 + q; };
 
     // Token columns r >= M repeat row M-1; their MFMA outputs are never used.
-    // x comes from L2 and is first needed at tile 0's MFMAs.  Loading it
-    // behind the weight prologue lets the stream start earlier (measured
-    // faster for every NKV: C1 6.92 -> 6.80 us, C3 0.12-0.26 us).
+    // x comes from L2 and is first needed at tile 0's MFMAs; where it goes
+    // in the prologue is chosen below.
     const int xrow = r < M ? r : M - 1;
     bf16x8 xv[ST];
     auto load_x = [&]() {
@@ -273,11 +273,16 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         }
     };
     static_assert(Sh::NB <= 4 && 3 * LD <= 63, "wait counts");
+    // Order of the first loads (the launch picks XFIRST for 12 or more
+    // token rows at NKV >= 4).
+    if constexpr (XFIRST)
+        load_x();
 #pragma unroll
     for (int t = 0; t < Sh::NB - 1; ++t)
         if (t < ub)
             issue(t);
-    load_x();
+    if constexpr (!XFIRST)
+        load_x();
 
     // The token's rotation for this lane's pair and the fault word, fetched
     // while W streams.  The barriers keep these loads behind the weight
@@ -465,12 +470,22 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     }
 }
 
+// x goes ahead of the weight prologue for 12 or more token rows at
+// NKV >= 4, behind it otherwise.  Measured on one box: x first took C4
+// 25.84 -> 25.60 us and NKV = 4 at M = 12 15.02 -> 14.87 us, but cost C3
+// 0.2 us and C1 0.1 us and changed nothing at NKV = 2; a runtime branch
+// choosing the order inside one kernel cost C3 0.5 us.
+template <int NKV>
+constexpr bool x_first_ok() { return NKV >= 4; }
+
 template <int NKV>
 hipError_t launch(int M, const void *x, const void *W, const int64_t *positions,
                   const int64_t *slots, const float *cos_sin, void *y, void *kv_cache,
                   unsigned *ws, bool coherent, unsigned spin_limit, hipStream_t stream)
 {
-    hipLaunchKernelGGL(front_fused<NKV>, dim3(kGrid), dim3(kWaves * 64), 0, stream,
+    auto kernel = x_first_ok<NKV>() && M >= 12 ? front_fused<NKV, x_first_ok<NKV>()>
+                                               : front_fused<NKV, false>;
+    hipLaunchKernelGGL(kernel, dim3(kGrid), dim3(kWaves * 64), 0, stream,
                        static_cast<const __bf16 *>(x), static_cast<const __bf16 *>(W),
                        positions, slots, cos_sin, static_cast<__bf16 *>(y),
                        static_cast<__bf16 *>(kv_cache), ws, M, coherent ? 1 : 0, spin_limit);
@@ -502,13 +517,15 @@ __global__ void __launch_bounds__(kWaves * 64) where_blocks_run(unsigned *out)
 template <int NKV>
 int occupancy()
 {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, front_fused<NKV>, kWaves * 64, 0) !=
-        hipSuccess) {
+    int n = 0, nx = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, front_fused<NKV, false>, kWaves * 64,
+                                                     0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nx, front_fused<NKV, x_first_ok<NKV>()>,
+                                                     kWaves * 64, 0) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
-    return n;
+    return n < nx ? n : nx;
 }
 
 }  // namespace
