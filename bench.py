@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--repeats", type=int, default=3, help="timed repeats; the median is kept")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and sweep point; one JSON line each on stderr")
+    ap.add_argument("--attn2-lines", action="store_true",
+                    help="only the attn2 lines of --all (stderr), then exit")
     ap.add_argument("--attn2", default="", metavar="WORKLOAD",
                     help="time attn2 instead of the front: one of " + ", ".join(wl.ATTN2_WORKLOADS))
     ap.add_argument("--attn2-batch-invariant", action="store_true",
@@ -806,6 +808,22 @@ def summarize_attn2_profiles(d: str, out: str | None = None) -> str:
     return table
 
 
+def attn2_all_lines(a) -> None:
+    """The attn2 part of the --all lines: one JSON line per timing workload on
+    stderr, with the oracle on this host."""
+    for aw in wl.ATTN2_WORKLOADS.values():
+        if aw is wl.A0:   # the small parity case, not a timing workload
+            continue
+        line = attn2_line(aw, a)
+        line["cpu_baseline"] = attn2_cpu_baseline(aw, a.all_cpu_seconds)
+        print(json.dumps({"workload": aw.name, "splits": line["config"]["splits"],
+                          "us_per_call": line["us_per_call"], "GB_per_s": line["value"],
+                          "frac_of_8TBs": line["roofline"]["frac"], "roofline": line["roofline"],
+                          "cpu_baseline": line["cpu_baseline"],
+                          "request_sets_rotated": line["config"]["request_sets_rotated"]}),
+              file=sys.stderr, flush=True)
+
+
 def all_lines(a) -> None:
     """One JSON line per workload and sweep point on stderr: timing, the
     roofline with counter traffic when recorded for this kernel source, and
@@ -837,17 +855,7 @@ def all_lines(a) -> None:
                           "frac_of_8TBs": ctx["frac_of_8TBs"],
                           "buffers_rotated": ctx["buffers_rotated"]}),
               file=sys.stderr, flush=True)
-    for aw in wl.ATTN2_WORKLOADS.values():
-        if aw is wl.A0:   # the small parity case, not a timing workload
-            continue
-        line = attn2_line(aw, a)
-        line["cpu_baseline"] = attn2_cpu_baseline(aw, a.all_cpu_seconds)
-        print(json.dumps({"workload": aw.name, "splits": line["config"]["splits"],
-                          "us_per_call": line["us_per_call"], "GB_per_s": line["value"],
-                          "frac_of_8TBs": line["roofline"]["frac"], "roofline": line["roofline"],
-                          "cpu_baseline": line["cpu_baseline"],
-                          "request_sets_rotated": line["config"]["request_sets_rotated"]}),
-              file=sys.stderr, flush=True)
+    attn2_all_lines(a)
     for lw in wl.LAYER_FRONT_WORKLOADS.values():
         line = layer_front_line(lw, a)
         line["cpu_baseline"] = layer_front_cpu_baseline(lw, a.all_cpu_seconds)
@@ -893,6 +901,9 @@ def main():
         line = layer_front_line(lw, a)
         line["cpu_baseline"] = layer_front_cpu_baseline(lw, a.cpu_baseline_seconds)
         print(json.dumps(line), flush=True)
+        return
+    if a.attn2_lines:
+        attn2_all_lines(a)
         return
     if a.attn2:
         if a.attn2 not in wl.ATTN2_WORKLOADS:
