@@ -164,9 +164,12 @@ const char *qkvf_strerror(int status);
 
 /*
  * The launch shape of (N, M): grid blocks of the projection kernel, the
- * split of K across blocks, waves per block and the most 16-row tiles a block
- * owns (each XCD owns whole heads, heads x * H / 8 .. (x + 1) * H / 8 - 1 of
- * the H = N / 64, and its 32 blocks share their tiles equally).
+ * split of K across blocks, waves per block and the most tiles of up to 16 W
+ * rows a block owns.  With 4 or 8 KV heads each XCD owns whole heads, heads
+ * x * H / 8 .. (x + 1) * H / 8 - 1 of the H = N / 64, and its 32 blocks share
+ * their tiles equally.  With 1 or 2 KV heads each XCD owns N / 8 rows (whole
+ * q and k heads, then v and gate rows) and every block 36 * nkv of them, as
+ * one tile of 4 or 8 rows and 16-row tiles: 3 or 5 tiles.
  * A pure function of its arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or
  * QKVF_ERR_ROWS.  Any output pointer may be NULL.
  */

@@ -6,11 +6,14 @@
 // does the whole call:
 //
 //  Projection: 256 blocks (one per CU, all resident together) of 8 waves.
-//    The heads (64 rows of W each, 18 per KV head) are shared out over the 8
-//    XCDs as whole heads, and the 32 blocks of an XCD split its heads' rows
-//    into S K ranges (S = 4 for 8 KV heads, else 8) and row groups: block b
-//    owns one K range of 8192/S and 2 to 9 row tiles of 16 W rows, so every
-//    partial it produces is read on its own XCD.  For each tile the block
+//    The rows of W (64 per head, 18 heads per KV head) are shared out over
+//    the 8 XCDs: as whole heads for 4 and 8 KV heads; for 1 and 2 KV heads,
+//    whose 18 or 36 heads do not divide by 8, as N / 8 rows per XCD (whole q
+//    and k heads, whose norm needs the whole head, filled up with v and gate
+//    rows).  The 32 blocks of an XCD split its rows into S K ranges (S = 4
+//    for 8 KV heads, else 8) and row groups: block b owns one K range of
+//    8192/S and 3 to 9 row tiles of up to 16 W rows, so every partial it
+//    produces is read on its own XCD.  For each tile the block
 //      - loads the 16 rows with non-temporal 16-byte loads straight into
 //        LDS (buffer loads with the lds bit), each wave instruction reading
 //        1 KB of one row (the shape HBM streams best), into a ring of 2 or 3
@@ -26,7 +29,8 @@
 //    the block's fp32 partials go to the workspace, one 32-bit word each.
 //
 //  Epilogue: each (head, pair of tokens) is one item of one wave, on the XCD
-//    whose blocks produced that head's partials.  The wave fetched its
+//    whose blocks produced that head's partials (with 1 or 2 KV heads the v
+//    and gate rows of an XCD form items of up to 64 columns instead).  The wave fetched its
 //    tokens' slots and cos|sin rows while the weights streamed; it reads the
 //    S partials of each of its columns until none is empty (a bounded wait,
 //    normally served by the XCD's own L2), sums them in split order, marks
@@ -101,8 +105,25 @@ struct Shape {
     // XCD x owns heads [x HEADS / 8, (x + 1) HEADS / 8); its 32 blocks take
     // the S splits of 32 / S row groups of those heads' tiles.
     static constexpr int MAX_HEADS = (HEADS + 7) / 8;
-    static constexpr int U_MAX = MAX_HEADS * 4 * S / 32;   // tiles per block, at most
+    // NKV <= 2 (H not a multiple of 8): balanced rows instead.  Only the q
+    // and k heads (NORM_HEADS, rows [0, 576 NKV)) need whole heads on one
+    // XCD, for their norm; the v and gate rows fill the rest, so every XCD
+    // owns ROWS_X = N / 8 rows.  Its 32 blocks take the S splits of GROUPS
+    // row groups of GROWS rows, as TPG tiles: tile 0 holds the group's
+    // first LAST rows, the others 16 each.  Every block then streams the
+    // same bytes.
+    static constexpr bool BAL = HEADS % 8 != 0;
+    static constexpr int NORM_HEADS = (kQPerKv + 1) * NKV;
+    static constexpr int ROWS_X = N / 8;
+    static constexpr int GROUPS = 32 / S;
+    static constexpr int GROWS = ROWS_X / GROUPS;
+    static constexpr int TPG = (GROWS + kTileRows - 1) / kTileRows;
+    static constexpr int LAST = GROWS - kTileRows * (TPG - 1);
+    static constexpr int U_MAX = BAL ? TPG : MAX_HEADS * 4 * S / 32;   // tiles per block, at most
     static_assert(KW % 32 == 0 && CHUNKS % 16 == 0, "whole MFMA steps, whole swizzle groups");
+    static_assert(!BAL || (GROWS * GROUPS == ROWS_X && LAST > 0 && LAST % 2 == 0 &&
+                           64 * ((NORM_HEADS + 7) / 8) <= ROWS_X),
+                  "whole row pairs per wave, every XCD's norm heads fit its rows");
     static_assert(LOADS * 64 == 2 * CHUNKS, "each wave loads exactly two tile rows");
     static_assert((HEADS / 8) * 4 * S % 32 == 0 && MAX_HEADS * 4 * S % 32 == 0, "whole tiles per block");
 };
@@ -184,21 +205,40 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     const int b = blockIdx.x;
     // Blocks are dispatched to the 8 XCDs round robin: block b runs on XCD
     // (b + c) % 8 for a c that varies between launches.  So the 32 blocks
-    // with b % 8 == x share one XCD; they own heads [x H / 8, (x + 1) H / 8)
-    // (H = 18 NKV heads: 2 or 3 heads each for NKV = 1, 4 or 5 for NKV = 2,
-    // 9 and 18 for NKV = 4 and 8) and take the S splits of 32 / S row groups
-    // of those heads' 16-row tiles, so the partials of a head never leave
-    // that XCD's L2.  Blocks of an XCD with more heads have more tiles: for
-    // NKV <= 2 that costs less than a hand-off between XCDs (measured: C1
-    // 8.41 -> 7.50 us, M = 16 at NKV = 1 9.61 -> 8.00 us, C2 10.17 -> 9.56 us
-    // against heads that straddle two XCDs with S = 32 / NKV).
+    // with b % 8 == x share one XCD; for NKV >= 4 they own heads
+    // [x H / 8, (x + 1) H / 8) (H = 18 NKV: 9 and 18 heads) and take the S
+    // splits of 32 / S row groups of those heads' 16-row tiles, so the
+    // partials of a head never leave that XCD's L2.  For NKV <= 2 whole
+    // heads would leave 2 of the 8 XCDs (NKV = 1) or 4 (NKV = 2) with a
+    // third or a quarter more rows; the balanced rows below give every
+    // block the same bytes, still with every partial read on its own XCD
+    // (measured on one box: C1 6.78 -> 6.46 us, M = 8 at NKV = 1 7.05 ->
+    // 6.74 us, C2 9.13 -> 9.02 us).
     const int xcd = b & 7;
     const int slot_in_xcd = b >> 3;
     const int split = slot_in_xcd % Sh::S;
     const int head_lo = xcd * Sh::HEADS / 8, head_hi = (xcd + 1) * Sh::HEADS / 8;
     // tiles of this block: a constant when every XCD has as many heads
-    const int ub = Sh::HEADS % 8 == 0 ? Sh::U_MAX : (head_hi - head_lo) * Sh::S / 8;
+    const int ub = Sh::HEADS % 8 == 0 || Sh::BAL ? Sh::U_MAX : (head_hi - head_lo) * Sh::S / 8;
     const int tile0 = head_lo * 4 + (slot_in_xcd / Sh::S) * ub;   // its first 16-row tile
+    // Balanced rows (NKV <= 2): this XCD's norm heads [nh_lo, nh_lo + nh),
+    // then its nn_cnt v and gate rows from nn_start; entry i of that list is
+    // W row list_row(i), and row group grp is entries [GROWS grp, + GROWS).
+    const int nh_lo = xcd * Sh::NORM_HEADS / 8;
+    const int nh = (xcd + 1) * Sh::NORM_HEADS / 8 - nh_lo;
+    const int nn_start = Sh::NORM_HEADS * kHeadDim + Sh::ROWS_X * xcd - kHeadDim * nh_lo;
+    const int nn_cnt = Sh::ROWS_X - kHeadDim * nh;
+    const int grp = slot_in_xcd / Sh::S;
+    auto list_row = [&](int i) {
+        return i < kHeadDim * nh ? kHeadDim * nh_lo + i : nn_start + i - kHeadDim * nh;
+    };
+    // Row offset and row count of tile t within the block's rows.
+    auto tile_off = [](int t) { return !Sh::BAL ? kTileRows * t : t == 0 ? 0 : Sh::LAST + kTileRows * (t - 1); };
+    auto tile_rows = [](int t) { return !Sh::BAL || t > 0 ? kTileRows : Sh::LAST; };
+    // W row (= y column) of row `row` of tile t.
+    auto w_row = [&](int t, int row) {
+        return Sh::BAL ? list_row(Sh::GROWS * grp + tile_off(t) + row) : (tile0 + t) * kTileRows + row;
+    };
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;   // A row (W row in the tile) and B column (token)
@@ -208,10 +248,19 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // This wave's epilogue item, if any: head `head` for tokens 2 tp (lanes
     // 0-31) and 2 tp + 1 (lanes 32-63), among this XCD's heads; lane pi of
     // each half owns rotation pair pi.
+    // With balanced rows the items are column groups: the XCD's norm heads,
+    // then its v and gate rows in runs of up to 64 columns (a run may end
+    // mid-head; lanes past its end read its last pair and store nothing).
     const int tpairs = (M + 1) >> 1;
     const int item = wave * (kGrid / 8) + slot_in_xcd;
-    const bool has_item = item < (head_hi - head_lo) * tpairs;
-    const int head = head_lo + (has_item ? item / tpairs : 0);
+    const int ngroups = Sh::BAL ? nh + (nn_cnt + kHeadDim - 1) / kHeadDim : head_hi - head_lo;
+    const bool has_item = item < ngroups * tpairs;
+    const int cg = has_item ? item / tpairs : 0;
+    const int head = head_lo + cg;
+    const int col0 = !Sh::BAL ? head * kHeadDim
+                     : cg < nh ? (nh_lo + cg) * kHeadDim
+                               : nn_start + (cg - nh) * kHeadDim;
+    const int ncols = !Sh::BAL || cg < nh ? kHeadDim : min(kHeadDim, nn_cnt - (cg - nh) * kHeadDim);
     const int tok = 2 * (has_item ? item % tpairs : 0) + (lane >> 5);
     const bool tok_ok = tok < M;
     const int tok_c = tok_ok ? tok : M - 1;  // keeps the idle half's loads in bounds
@@ -254,10 +303,16 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const int row = 2 * wave + (j * 64) / C;
             const int c0 = (j * 64) % C;
             const int loff = (row * C + c0) * 16;
-            const int goff = (row * kHidden + (c0 + (lane ^ (row & 15))) * 8) * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (__attribute__((address_space(3))) void *)(bufp(t % Sh::NB) + loff), 16,
-                wtile + t * kTileBytes + goff, 0, 0, kCacheNt);
+            const int coff = (c0 + (lane ^ (row & 15))) * 16;
+            // Balanced rows are gathered from the XCD's list; a short tile 0
+            // has no rows for the later waves (wave-uniform), and being the
+            // first tile it never sits behind a wait for another.
+            const int voff = Sh::BAL ? (w_row(t, row) * kHidden + k0) * 2 + coff
+                                     : wtile + t * kTileBytes + row * kHidden * 2 + coff;
+            if (tile_rows(t) == kTileRows || row < tile_rows(t))
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, (__attribute__((address_space(3))) void *)(bufp(t % Sh::NB) + loff), 16,
+                    voff, 0, 0, kCacheNt);
         }
     };
     // Wait until at most `later` tiles of this wave's loads are in flight
@@ -288,10 +343,24 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // while W streams.  The barriers keep these loads behind the weight
     // prologue, so waiting for them never stalls the stream; both are first
     // needed after the stream.
+    // With balanced rows (NKV <= 2) the short tile 0 is loaded by some waves
+    // only, so the compiler cannot count this wave's loads exactly and would
+    // wait here for most of tile 0 before the position arrives; there the
+    // rotation is fetched once tile 0 has landed (in the loop below).
     __builtin_amdgcn_sched_barrier(0);
-    const float *cs_row = cos_sin != nullptr ? cos_sin + pos_t * kHeadDim
-                                             : reinterpret_cast<const float *>(ws);
-    float rc = cs_row[pi], rs = cs_row[32 + pi];
+    float rc = 0.f, rs = 0.f;
+    auto load_rotation = [&]() {
+        // An opaque copy of the position: the compiler would otherwise
+        // compute the row's address (and wait for the position) early.
+        int64_t pos_u;
+        asm volatile("" : "=v"(pos_u) : "0"(pos_t));
+        const float *cs_row = cos_sin != nullptr ? cos_sin + pos_u * kHeadDim
+                                                 : reinterpret_cast<const float *>(ws);
+        rc = cs_row[pi];
+        rs = cs_row[32 + pi];
+    };
+    if constexpr (!Sh::BAL)
+        load_rotation();
     const unsigned fault_v =
         __hip_atomic_load(ws + kFaultWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_sched_barrier(0);
@@ -308,7 +377,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     auto store_partial = [&](float sum, int u, int t, int row) {
         unsigned bits = __float_as_uint(sum);
         bits = bits == kPartialEmpty ? kPartialNan : bits;
-        const int n = (tile0 + u) * kTileRows + row;
+        const int n = w_row(u, row);
         unsigned *dst = parts + (size_t(split) * M + t) * N + n;
         // The reader of row n runs on this XCD: a plain store is enough (the
         // reader's device-coherent load is served by the shared L2).
@@ -345,12 +414,14 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             block_barrier();
         if (u + Sh::NB - 1 < ub)
             issue(u + Sh::NB - 1);
-        if (u > 0 && summer)
+        if (u > 0 && summer && (threadIdx.x & 15) < tile_rows(u - 1))
             store_partial(block_sum(red[(u - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
                           u - 1, threadIdx.x >> 4, threadIdx.x & 15);
         // This wave's loads of tile u have landed, then everyone's have.
         wait_tiles(min(u + Sh::NB - 1, ub - 1) - u);
         block_barrier();
+        if (Sh::BAL && u == 0)
+            load_rotation();
         const unsigned char *tile = bufp(u % Sh::NB);
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -366,7 +437,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         }
     }
     __syncthreads();
-    if (summer)
+    if (summer && (threadIdx.x & 15) < tile_rows(ub - 1))
         store_partial(block_sum(red[(ub - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
                       ub - 1, threadIdx.x >> 4, threadIdx.x & 15);
 
@@ -385,7 +456,8 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         // The S partials of this lane's two columns: poll (bounded) with
         // device-coherent loads until none is empty, then sum in split order
         // and empty them for the next call.
-        const int n = head * kHeadDim + 2 * pi;
+        const bool pair_ok = 2 * pi < ncols;
+        const int n = col0 + min(2 * pi, ncols - 2);
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             parts, 0, int(sizeof(unsigned) * kPartialWords), kBufferConfig);
         const int base = (tok_c * N + n) * int(sizeof(unsigned));
@@ -423,10 +495,11 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             a1 += __uint_as_float(v[sp].y);
         }
         // Empty the words for the next call (the lanes of a token past M read
-        // token M - 1's words too, and leave them to that token's lanes).  A
-        // wave that gave up leaves them: the fault state stops later calls.
+        // token M - 1's words too, and lanes past a run's end its last pair;
+        // both leave them to their own lanes).  A wave that gave up leaves
+        // them: the fault state stops later calls.
         asm volatile("" ::: "memory");
-        if (tok_ok && !gave_up) {
+        if (tok_ok && pair_ok && !gave_up) {
             unsigned char *pb = reinterpret_cast<unsigned char *>(parts) + base;
 #pragma unroll
             for (int sp = 0; sp < Sh::S; ++sp)
@@ -443,7 +516,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             rc = 1.f;
             rs = 0.f;
         }
-        const int h = head;
+        const int h = n / kHeadDim;   // the item's head, or one of a run's two
         __bf16 o0 = p0, o1 = p1;
         if (h < NQ + NKV) {  // q and k heads
             const float rr = rsqrtf(ss * (1.0f / kHeadDim) + kEps);
@@ -455,7 +528,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         // A wave that gave up holds stale sums: it stores nothing, so the
         // cache never receives them (its y and cache entries keep their old
         // contents and the fault word says the call failed).
-        const bool store = tok_ok && !gave_up;
+        const bool store = tok_ok && pair_ok && !gave_up;
         if (store)
             *reinterpret_cast<unsigned *>(y + size_t(tok) * N + n) = packed;
 
@@ -464,7 +537,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const bool is_k = h < NQ + NKV;
             const int j = is_k ? h - NQ : h - NQ - NKV;
             __bf16 *dst = kv_cache + ((page * NKV + j) * kPageSlots + off) * kSlotWidth +
-                          (is_k ? 0 : kHeadDim) + 2 * pi;
+                          (is_k ? 0 : kHeadDim) + n % kHeadDim;
             *reinterpret_cast<unsigned *>(dst) = packed;
         }
     }

@@ -59,13 +59,20 @@ def test_plan_is_a_function_of_shape(L, nkv):
         p = qf.plan(N, M)
         S = 4 if nkv == 8 else 8
         H = N // 64
-        heads = [(x + 1) * H // 8 - x * H // 8 for x in range(8)]
-        tiles = [h * 4 * S // 32 for h in heads]       # per block on XCD x
-        assert all(h * 4 * S % 32 == 0 for h in heads)
+        if nkv >= 4:
+            # whole heads per XCD; its 32 blocks share their 16-row tiles
+            heads = [(x + 1) * H // 8 - x * H // 8 for x in range(8)]
+            tiles = [h * 4 * S // 32 for h in heads]       # per block on XCD x
+            assert all(h * 4 * S % 32 == 0 for h in heads)
+            # every W row tile and every K split is covered exactly once
+            assert sum(32 * t for t in tiles) == (N // 16) * S
+        else:
+            # N / 8 rows per XCD, 36 nkv per block: a short tile, then 16-row tiles
+            rows = N // 8 // (32 // S)
+            assert rows == 36 * nkv and 8 * (32 // S) * rows == N
+            tiles = [-(-rows // 16)]
         assert p == {"grid": 256, "k_splits": S, "waves_per_block": 8,
                      "tiles_per_block": max(tiles)}
-        # every W row tile and every K split is covered exactly once
-        assert sum(32 * t for t in tiles) == (N // 16) * S
         assert max(tiles) == {1: 3, 2: 5, 4: 9, 8: 9}[nkv]
 
 
