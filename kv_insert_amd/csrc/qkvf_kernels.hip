@@ -329,7 +329,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     };
     static_assert(Sh::NB <= 4 && 3 * LD <= 63, "wait counts");
     // Order of the first loads (the launch picks XFIRST for 12 or more
-    // token rows at NKV >= 4).
+    // token rows).
     if constexpr (XFIRST)
         load_x();
 #pragma unroll
@@ -543,21 +543,20 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     }
 }
 
-// x goes ahead of the weight prologue for 12 or more token rows at
-// NKV >= 4, behind it otherwise.  Measured on one box: x first took C4
-// 25.84 -> 25.60 us and NKV = 4 at M = 12 15.02 -> 14.87 us, but cost C3
-// 0.2 us and C1 0.1 us and changed nothing at NKV = 2; a runtime branch
-// choosing the order inside one kernel cost C3 0.5 us.
-template <int NKV>
-constexpr bool x_first_ok() { return NKV >= 4; }
+// x goes ahead of the weight prologue for 12 or more token rows, behind it
+// otherwise.  Measured on one box: x first took C4 25.84 -> 25.60 us, NKV =
+// 4 at M = 12 15.02 -> 14.87 us and, with the balanced rows, NKV = 2 at M =
+// 16 9.60 -> 9.42 us, but cost C3 0.2 us and C1 0.1 us (and NKV = 1 at M =
+// 4 and 8 about 0.1 us); a runtime branch choosing the order inside one
+// kernel cost C3 0.5 us.
+constexpr int kXFirstRows = 12;
 
 template <int NKV>
 hipError_t launch(int M, const void *x, const void *W, const int64_t *positions,
                   const int64_t *slots, const float *cos_sin, void *y, void *kv_cache,
                   unsigned *ws, bool coherent, unsigned spin_limit, hipStream_t stream)
 {
-    auto kernel = x_first_ok<NKV>() && M >= 12 ? front_fused<NKV, x_first_ok<NKV>()>
-                                               : front_fused<NKV, false>;
+    auto kernel = M >= kXFirstRows ? front_fused<NKV, true> : front_fused<NKV, false>;
     hipLaunchKernelGGL(kernel, dim3(kGrid), dim3(kWaves * 64), 0, stream,
                        static_cast<const __bf16 *>(x), static_cast<const __bf16 *>(W),
                        positions, slots, cos_sin, static_cast<__bf16 *>(y),
@@ -593,7 +592,7 @@ int occupancy()
     int n = 0, nx = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, front_fused<NKV, false>, kWaves * 64,
                                                      0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nx, front_fused<NKV, x_first_ok<NKV>()>,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nx, front_fused<NKV, true>,
                                                      kWaves * 64, 0) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
