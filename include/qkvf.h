@@ -168,8 +168,10 @@ const char *qkvf_strerror(int status);
  * rows a block owns.  With 4 or 8 KV heads each XCD owns whole heads, heads
  * x * H / 8 .. (x + 1) * H / 8 - 1 of the H = N / 64, and its 32 blocks share
  * their tiles equally.  With 1 or 2 KV heads each XCD owns N / 8 rows (whole
- * q and k heads, then v and gate rows) and every block 36 * nkv of them, as
- * one tile of 4 or 8 rows and 16-row tiles: 3 or 5 tiles.
+ * q and k heads, then v and gate rows) and every block an equal share of
+ * them, as one short tile and 16-row tiles: 36 rows in 3 tiles with 1 KV
+ * head, and with 2 KV heads 72 rows in 5 tiles (8 K splits) from 12 token
+ * rows, 36 rows in 3 tiles (4 K splits, 2048 K each) below.
  * A pure function of its arguments.  Returns QKVF_OK, QKVF_ERR_SHAPE or
  * QKVF_ERR_ROWS.  Any output pointer may be NULL.
  */

@@ -338,12 +338,12 @@ int qkvf_plan(int N, int M, int *grid, int *k_splits, int *waves_per_block, int 
     if (M < 1 || M > kMaxRows)
         return QKVF_ERR_ROWS;
     if (grid) *grid = kGrid;
-    if (k_splits) *k_splits = splits_for(nkv);
+    if (k_splits) *k_splits = splits_for(nkv, M);
     if (waves_per_block) *waves_per_block = kWaves;
     if (tiles_per_block) {
         int most = 0;
         for (int x = 0; x < 8; ++x)
-            most = std::max(most, tiles_for(nkv, x));
+            most = std::max(most, tiles_for(nkv, M, x));
         *tiles_per_block = most;
     }
     return QKVF_OK;

@@ -22,20 +22,24 @@ constexpr int kGrid = 256;          // projection blocks: one per CU
 
 // Columns for nkv KV heads: [q | k | v | gate] = 2 * (8 + 1) * nkv heads.
 constexpr int cols_for(int nkv) { return 2 * (kQPerKv + 1) * nkv * kHeadDim; }
+// Token rows from which x is loaded ahead of the weights; below it, with 2
+// KV heads, K is split 4 ways instead of 8 (the launch picks the kernel).
+constexpr int kXFirstRows = 12;
+constexpr bool wide_splits(int nkv, int M) { return nkv == 2 && M < kXFirstRows; }
 // K split across blocks.  For nkv >= 4 each XCD owns whole heads (18 nkv / 8
 // of them) and its 32 blocks take the splits of 32 / splits row groups of
 // those heads' 16-row tiles.  For nkv <= 2 (18 nkv heads do not divide by 8)
 // each XCD owns N / 8 rows: whole q and k heads (their norm needs the whole
-// head) filled up with v and gate rows, in 32 / splits row groups of 36 nkv
-// rows; a block's tiles are one short tile (4 or 8 rows) and 16-row tiles.
-constexpr int splits_for(int nkv) { return nkv == 8 ? 4 : 8; }
+// head) filled up with v and gate rows, in 32 / splits row groups; a
+// block's tiles are one short tile and 16-row tiles.
+constexpr int splits_for(int nkv, int M) { return nkv == 8 || wide_splits(nkv, M) ? 4 : 8; }
 // Heads of XCD x: [x heads / 8, (x + 1) heads / 8), heads = 18 nkv.
 constexpr int xcd_heads(int nkv, int x) { return (x + 1) * 18 * nkv / 8 - x * 18 * nkv / 8; }
 // Tiles of a block on XCD x (the same on every XCD for nkv <= 2).
-constexpr int tiles_for(int nkv, int x)
+constexpr int tiles_for(int nkv, int M, int x)
 {
-    return nkv <= 2 ? (36 * nkv + kTileRows - 1) / kTileRows
-                    : xcd_heads(nkv, x) * 4 * splits_for(nkv) / (kGrid / 8);
+    return nkv <= 2 ? (144 * nkv / (32 / splits_for(nkv, M)) + kTileRows - 1) / kTileRows
+                    : xcd_heads(nkv, x) * 4 * splits_for(nkv, M) / (kGrid / 8);
 }
 
 // Workspace layout (32-bit words): partials [splits][M][N], one fp32 word

@@ -87,11 +87,13 @@ constexpr int kCacheNt = 2;
 
 constexpr float kEps = 1e-6f;
 
-template <int NKV>
+// WIDE: K split 4 ways instead of 8 with the balanced rows (2 KV heads below
+// kXFirstRows token rows, chosen at launch).
+template <int NKV, bool WIDE = false>
 struct Shape {
     static constexpr int N = cols_for(NKV);
     static constexpr int HEADS = N / kHeadDim;     // 18 per KV head
-    static constexpr int S = NKV == 8 ? 4 : 8;     // K splits across blocks
+    static constexpr int S = NKV == 8 || WIDE ? 4 : 8;   // K splits across blocks
     static constexpr int KB = kHidden / S;         // K per block
     static constexpr int KW = KB / kWaves;         // K per wave
     static constexpr int STEPS = KW / 32;          // MFMA K steps per tile and wave
@@ -101,7 +103,7 @@ struct Shape {
     // Tiles in the LDS ring: measured on one box against rings of 2, 3 and
     // 4 tiles (C1 6.87 / 7.03 / 7.12 us, C2 9.13 at 2 or 3 against 10.04 at
     // 4, nkv = 4 at M = 1 14.35 / 14.10 / 14.36 us); 64 KB tiles allow 2.
-    static constexpr int NB = NKV == 1 || NKV == 8 ? 2 : 3;
+    static constexpr int NB = NKV == 1 || NKV == 8 || WIDE ? 2 : 3;
     // XCD x owns heads [x HEADS / 8, (x + 1) HEADS / 8); its 32 blocks take
     // the S splits of 32 / S row groups of those heads' tiles.
     static constexpr int MAX_HEADS = (HEADS + 7) / 8;
@@ -125,7 +127,9 @@ struct Shape {
                            64 * ((NORM_HEADS + 7) / 8) <= ROWS_X),
                   "whole row pairs per wave, every XCD's norm heads fit its rows");
     static_assert(LOADS * 64 == 2 * CHUNKS, "each wave loads exactly two tile rows");
-    static_assert((HEADS / 8) * 4 * S % 32 == 0 && MAX_HEADS * 4 * S % 32 == 0, "whole tiles per block");
+    static_assert(BAL || ((HEADS / 8) * 4 * S % 32 == 0 && MAX_HEADS * 4 * S % 32 == 0),
+                  "whole tiles per block");
+    static_assert(!WIDE || BAL, "4-way splits only with the balanced rows");
 };
 
 __device__ inline bf16x8 load16(const __bf16 *p)
@@ -167,8 +171,9 @@ __device__ inline unsigned pack2(__bf16 lo, __bf16 hi)
            (unsigned(__builtin_bit_cast(unsigned short, hi)) << 16);
 }
 
-// XFIRST: x is loaded ahead of the weight prologue (chosen at launch).
-template <int NKV, bool XFIRST>
+// XFIRST: x is loaded ahead of the weight prologue; WIDE: see Shape (both
+// chosen at launch).
+template <int NKV, bool XFIRST, bool WIDE>
 __global__ void __launch_bounds__(kWaves * 64, 1)
 front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const int64_t *__restrict__ positions, const int64_t *__restrict__ slots,
@@ -176,7 +181,7 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             __bf16 *__restrict__ kv_cache, unsigned *__restrict__ ws, int M, int coherent,
             unsigned spin_limit)
 {
-    using Sh = Shape<NKV>;
+    using Sh = Shape<NKV, WIDE>;
     constexpr int ST = Sh::STEPS, U = Sh::U_MAX, C = Sh::CHUNKS;
     constexpr int LD = Sh::LOADS, N = Sh::N, NQ = kQPerKv * NKV;
     constexpr size_t kTileStride = size_t(kTileRows) * kHidden;
@@ -543,20 +548,24 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     }
 }
 
-// x goes ahead of the weight prologue for 12 or more token rows, behind it
-// otherwise.  Measured on one box: x first took C4 25.84 -> 25.60 us, NKV =
-// 4 at M = 12 15.02 -> 14.87 us and, with the balanced rows, NKV = 2 at M =
-// 16 9.60 -> 9.42 us, but cost C3 0.2 us and C1 0.1 us (and NKV = 1 at M =
-// 4 and 8 about 0.1 us); a runtime branch choosing the order inside one
-// kernel cost C3 0.5 us.
-constexpr int kXFirstRows = 12;
+// x goes ahead of the weight prologue for kXFirstRows (12) or more token
+// rows, behind it otherwise.  Measured on one box: x first took C4 25.84 ->
+// 25.60 us, NKV = 4 at M = 12 15.02 -> 14.87 us and, with the balanced rows,
+// NKV = 2 at M = 16 9.60 -> 9.42 us, but cost C3 0.2 us and C1 0.1 us (and
+// NKV = 1 at M = 4 and 8 about 0.1 us); a runtime branch choosing the order
+// inside one kernel cost C3 0.5 us.  Below 12 rows NKV = 2 splits K 4 ways
+// (wide_splits): 0.05-0.15 us faster at M = 1 ... 8 (fewer, larger tiles and
+// half the partials), 0.25 us slower at M = 12 and 0.3 us at M = 16, where
+// each block's x doubles; at NKV = 1 slower at every M.
 
 template <int NKV>
 hipError_t launch(int M, const void *x, const void *W, const int64_t *positions,
                   const int64_t *slots, const float *cos_sin, void *y, void *kv_cache,
                   unsigned *ws, bool coherent, unsigned spin_limit, hipStream_t stream)
 {
-    auto kernel = M >= kXFirstRows ? front_fused<NKV, true> : front_fused<NKV, false>;
+    auto kernel = M >= kXFirstRows          ? front_fused<NKV, true, false>
+                  : wide_splits(NKV, M) ? front_fused<NKV, false, NKV == 2>
+                                        : front_fused<NKV, false, false>;
     hipLaunchKernelGGL(kernel, dim3(kGrid), dim3(kWaves * 64), 0, stream,
                        static_cast<const __bf16 *>(x), static_cast<const __bf16 *>(W),
                        positions, slots, cos_sin, static_cast<__bf16 *>(y),
@@ -589,15 +598,17 @@ __global__ void __launch_bounds__(kWaves * 64) where_blocks_run(unsigned *out)
 template <int NKV>
 int occupancy()
 {
-    int n = 0, nx = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, front_fused<NKV, false>, kWaves * 64,
-                                                     0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nx, front_fused<NKV, true>,
+    int n = 0, nx = 0, nw = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, front_fused<NKV, false, false>,
+                                                     kWaves * 64, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nx, front_fused<NKV, true, false>,
+                                                     kWaves * 64, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nw, front_fused<NKV, false, NKV == 2>,
                                                      kWaves * 64, 0) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
-    return n < nx ? n : nx;
+    return n < nx ? (n < nw ? n : nw) : (nx < nw ? nx : nw);
 }
 
 }  // namespace
