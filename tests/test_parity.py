@@ -53,6 +53,19 @@ def test_sweep_parity(nkv, M):
     check(case, g)
 
 
+@pytest.mark.parametrize("nkv", [1, 2])
+@pytest.mark.parametrize("M", [6, 7, 9, 10, 11, 13, 14, 15])
+def test_balanced_rows_other_token_counts(nkv, M):
+    """The row counts the sweep skips, with 1 and 2 KV heads: balanced rows
+    per XCD, whose v and gate readers take runs of columns that end inside a
+    head; odd M leaves half a reader wave idle; 2 KV heads switch from 4 to
+    8 K splits (and x ahead of the weights) between 11 and 12 rows."""
+    w = wl.sweep(M, nkv)
+    case = Case(w, W=_sweep_weights(nkv))
+    g = run_gpu(case)
+    check(case, g)
+
+
 @pytest.mark.parametrize("nkv", [1, 8])
 def test_edge_positions_and_slots(nkv):
     """First and last table rows, first and last cache slots, page edges."""
