@@ -101,11 +101,13 @@ struct Shape {
     static constexpr int LOADS = 2 * CHUNKS / 64;  // 1 KB loads per wave per tile (2 rows)
     static constexpr int TILE_BYTES = kTileRows * KB * 2;
     // Tiles in the LDS ring: measured on one box against rings of 2, 3 and
-    // 4 tiles (C1 6.87 / 7.03 / 7.12 us, C2 9.13 at 2 or 3 against 10.04 at
-    // 4, nkv = 4 at M = 1 14.35 / 14.10 / 14.36 us); 64 KB tiles allow 2.
+    // 4 tiles (with whole heads: C1 6.87 / 7.03 / 7.12 us, C2 9.13 at 2 or 3
+    // against 10.04 at 4, nkv = 4 at M = 1 14.35 / 14.10 / 14.36 us; with the
+    // balanced rows 3 tiles at NKV = 1 and 4 at NKV = 2 were slower again);
+    // 64 KB tiles allow 2.
     static constexpr int NB = NKV == 1 || NKV == 8 || WIDE ? 2 : 3;
-    // XCD x owns heads [x HEADS / 8, (x + 1) HEADS / 8); its 32 blocks take
-    // the S splits of 32 / S row groups of those heads' tiles.
+    // NKV >= 4: XCD x owns heads [x HEADS / 8, (x + 1) HEADS / 8); its 32
+    // blocks take the S splits of 32 / S row groups of those heads' tiles.
     static constexpr int MAX_HEADS = (HEADS + 7) / 8;
     // NKV <= 2 (H not a multiple of 8): balanced rows instead.  Only the q
     // and k heads (NORM_HEADS, rows [0, 576 NKV)) need whole heads on one
@@ -238,11 +240,14 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
         return i < kHeadDim * nh ? kHeadDim * nh_lo + i : nn_start + i - kHeadDim * nh;
     };
     // Row offset and row count of tile t within the block's rows.
-    auto tile_off = [](int t) { return !Sh::BAL ? kTileRows * t : t == 0 ? 0 : Sh::LAST + kTileRows * (t - 1); };
+    auto tile_off = [](int t) {
+        return !Sh::BAL ? kTileRows * t : t == 0 ? 0 : Sh::LAST + kTileRows * (t - 1);
+    };
     auto tile_rows = [](int t) { return !Sh::BAL || t > 0 ? kTileRows : Sh::LAST; };
     // W row (= y column) of row `row` of tile t.
     auto w_row = [&](int t, int row) {
-        return Sh::BAL ? list_row(Sh::GROWS * grp + tile_off(t) + row) : (tile0 + t) * kTileRows + row;
+        return Sh::BAL ? list_row(Sh::GROWS * grp + tile_off(t) + row)
+                       : (tile0 + t) * kTileRows + row;
     };
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -404,9 +409,9 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     // needed.
     //
     // Per tile u: a barrier frees the buffer of tile u - 1, tile u + NB - 1
-    // is sent into it, the sum of tile u - 1 is stored, and after this
-    // wave's loads of tile u have landed a second barrier waits for every
-    // wave's; then the MFMAs read tile u from LDS.
+    // is sent into it, the sum of tile u - 1 is taken, and after this wave's
+    // loads of tile u have landed a second barrier waits for every wave's;
+    // then the sum is stored and the MFMAs read tile u from LDS.
     __shared__ float red[2][SLAB];
     const bool summer = threadIdx.x < kTileRows * M;
 #pragma unroll
@@ -419,12 +424,19 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             block_barrier();
         if (u + Sh::NB - 1 < ub)
             issue(u + Sh::NB - 1);
-        if (u > 0 && summer && (threadIdx.x & 15) < tile_rows(u - 1))
-            store_partial(block_sum(red[(u - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15),
-                          u - 1, threadIdx.x >> 4, threadIdx.x & 15);
+        const bool sum_prev = u > 0 && summer && (threadIdx.x & 15) < tile_rows(u - 1);
+        float prev = 0.f;
+        if (sum_prev)
+            prev = block_sum(red[(u - 1) & 1], threadIdx.x >> 4, threadIdx.x & 15);
         // This wave's loads of tile u have landed, then everyone's have.
         wait_tiles(min(u + Sh::NB - 1, ub - 1) - u);
         block_barrier();
+        // The sum of tile u - 1 is stored after the wait: stores count with
+        // loads, so a store issued before it would be waited for too (at
+        // the last tile, whose wait is for everything, that exposed the
+        // store's round trip once the tile itself had landed early).
+        if (sum_prev)
+            store_partial(prev, u - 1, threadIdx.x >> 4, threadIdx.x & 15);
         if (Sh::BAL && u == 0)
             load_rotation();
         const unsigned char *tile = bufp(u % Sh::NB);
