@@ -153,14 +153,17 @@ def test_front_beside_a_large_copy_on_another_stream():
     torch.cuda.empty_cache()
 
 
-def test_alternating_row_counts_leave_no_stale_partials():
-    """Row counts 16, 1, 7, 16, 3, 16 one after another on one stream: each
-    uses its own positions in the workspace, so a partial left full by one
-    call would be taken by a later one.  Every call must equal the same call
-    made alone."""
-    w = wl.sweep(16, 8)
+@pytest.mark.parametrize("nkv, rows", [(8, [16, 1, 7, 16, 3, 16]),
+                                       (2, [16, 1, 11, 12, 7, 16, 3])],
+                         ids=["nkv8", "nkv2_split_switch"])
+def test_alternating_row_counts_leave_no_stale_partials(nkv, rows):
+    """Row counts one after another on one stream: each uses its own
+    positions in the workspace (with 2 KV heads also its own split count, 4
+    below 12 rows and 8 from 12), so a partial left full by one call would
+    be taken by a later one.  Every call must equal the same call made
+    alone."""
+    w = wl.sweep(16, nkv)
     W = wl.make_weights(w, 0)
-    rows = [16, 1, 7, 16, 3, 16]
     cases = {m: Case(w, M=m, W=W) for m in set(rows)}
     alone = {}
     for m, c in cases.items():
@@ -178,4 +181,4 @@ def test_alternating_row_counts_leave_no_stale_partials():
     assert qf.device_fault() == 0
     for m, g in outs:
         assert torch.equal(g["y"].view(torch.int16), alone[m].view(torch.int16)), m
-    check(cases[16], outs[-1][1])
+    check(cases[outs[-1][0]], outs[-1][1])   # the last call against the oracle
