@@ -31,7 +31,8 @@ def _static(case, g):
 @pytest.mark.parametrize("first,second", [
     (wl.sweep(16, 8), wl.sweep(3, 8)),      # fewer tokens
     (wl.C3, wl.C1),                         # fewer tokens and fewer KV heads
-], ids=["m16_then_m3", "c3_then_c1"])
+    (wl.sweep(16, 2), wl.C2),               # 2 KV heads: 8 K splits, then 4
+], ids=["m16_then_m3", "c3_then_c1", "nkv2_m16_then_m8"])
 def test_static_entry_matches_run_twice_in_a_row(first, second):
     a, b = Case(first), Case(second)
     ref_a = run_gpu(a, label=f"qkvf_run {first.name}")
