@@ -10,10 +10,12 @@
 //    the 8 XCDs: as whole heads for 4 and 8 KV heads; for 1 and 2 KV heads,
 //    whose 18 or 36 heads do not divide by 8, as N / 8 rows per XCD (whole q
 //    and k heads, whose norm needs the whole head, filled up with v and gate
-//    rows).  The 32 blocks of an XCD split its rows into S K ranges (S = 4
-//    for 8 KV heads, else 8) and row groups: block b owns one K range of
-//    8192/S and 3 to 9 row tiles of up to 16 W rows, so every partial it
-//    produces is read on its own XCD.  For each tile the block
+//    rows).  The 32 blocks of an XCD split its rows into S K splits (S = 4
+//    for 8 KV heads and for 2 below 12 token rows, else 8) and row groups:
+//    block b owns one split of 8192/S K values (a contiguous range with 8 KV
+//    heads, interleaved 1 KB pieces otherwise) and 3 to 9 row tiles of up
+//    to 16 W rows, so every partial it produces is read on its own XCD.  For
+//    each tile the block
 //      - loads the 16 rows with non-temporal 16-byte loads straight into
 //        LDS (buffer loads with the lds bit), each wave instruction reading
 //        1 KB of one row (the shape HBM streams best), into a ring of 2 or 3
@@ -253,7 +255,17 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;   // A row (W row in the tile) and B column (token)
     const int q = lane >> 4;   // which 8 of the 32 K values of a step
-    const int k0 = split * Sh::KB;
+    // Global 16-byte chunk (of a W row, or of x) of the block's chunk c.
+    // With 8 KV heads a split is one contiguous K range.  With 1-4 KV heads
+    // the S splits take interleaved 1 KB pieces instead (split s owns pieces
+    // s, s + S, ... of every row), so sibling blocks working in step read
+    // whole stretches of a row together.  Measured on one box, alternating
+    // two rounds: nkv = 4 at M = 16 15.25 -> 14.80 us, at M = 1 and 8
+    // 0.12-0.16 us faster, nkv = 2 0.06-0.13 us and nkv = 1 up to 0.07 us;
+    // at 8 KV heads C4 was 0.15 us slower and C3 unchanged.
+    auto gchunk = [&](int c) {
+        return NKV <= 4 ? ((c >> 6) * Sh::S + split) * 64 + (c & 63) : split * Sh::CHUNKS + c;
+    };
 
     // This wave's epilogue item, if any: head `head` for tokens 2 tp (lanes
     // 0-31) and 2 tp + 1 (lanes 32-63), among this XCD's heads; lane pi of
@@ -279,9 +291,9 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     const int64_t pos_t = positions[tok_c];
     const int64_t slot_t = slots[tok_c];
 
-    // Chunk (8 K values) of this lane's operands in MFMA step st, relative to
-    // k0: A (W) and B (x) use the same chunk, so the MFMA contracts matching
-    // K values.
+    // Chunk (8 K values) of this lane's operands in MFMA step st, among the
+    // block's chunks (gchunk gives its place in the row): A (W) and B (x)
+    // use the same chunk, so the MFMA contracts matching K values.
     auto chunk_of = [&](int st) { return wave * 4 * ST + st * 4 + q; };
 
     // Token columns r >= M repeat row M-1; their MFMA outputs are never used.
@@ -292,14 +304,14 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
     auto load_x = [&]() {
 #pragma unroll
         for (int st = 0; st < ST; ++st)
-            xv[st] = load16(x + size_t(xrow) * kHidden + k0 + chunk_of(st) * 8);
+            xv[st] = load16(x + size_t(xrow) * kHidden + gchunk(chunk_of(st)) * 8);
     };
 
     // Byte offsets into W, which is at most 9216 x 8192 bf16 (151 MB).
     static_assert(size_t(N) * kHidden * 2 < (size_t(1) << 31), "W offsets fit 31 bits");
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(W), 0, int(size_t(N) * kHidden * 2), kBufferConfig);
-    const int wtile = int((size_t(tile0 * kTileRows) * kHidden + k0) * 2);
+    const int wtile = int((size_t(tile0 * kTileRows) * kHidden) * 2);
     constexpr int kTileBytes = int(kTileStride * 2);
     // Tile t goes straight into LDS ring buffer t % NB.  Load j of a wave
     // covers 64 consecutive chunks c0 .. c0 + 63 of tile row `row` (rows 2w,
@@ -313,11 +325,11 @@ front_fused(const __bf16 *__restrict__ x, const __bf16 *__restrict__ W,
             const int row = 2 * wave + (j * 64) / C;
             const int c0 = (j * 64) % C;
             const int loff = (row * C + c0) * 16;
-            const int coff = (c0 + (lane ^ (row & 15))) * 16;
+            const int coff = gchunk(c0 + (lane ^ (row & 15))) * 16;
             // Balanced rows are gathered from the XCD's list; a short tile 0
             // has no rows for the later waves (wave-uniform), and being the
             // first tile it never sits behind a wait for another.
-            const int voff = Sh::BAL ? (w_row(t, row) * kHidden + k0) * 2 + coff
+            const int voff = Sh::BAL ? (w_row(t, row) * kHidden) * 2 + coff
                                      : wtile + t * kTileBytes + row * kHidden * 2 + coff;
             if (tile_rows(t) == kTileRows || row < tile_rows(t))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
