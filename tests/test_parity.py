@@ -44,8 +44,9 @@ def _sweep_weights(nkv):
     return _W_BY_NKV[nkv]
 
 
-@pytest.mark.parametrize("nkv", wl.SWEEP_NKV)
+# nkv is the inner parameter, so consecutive cases share one weight set.
 @pytest.mark.parametrize("M", wl.SWEEP_M)
+@pytest.mark.parametrize("nkv", wl.SWEEP_NKV)
 def test_sweep_parity(nkv, M):
     w = wl.sweep(M, nkv)
     case = Case(w, W=_sweep_weights(nkv))
@@ -53,13 +54,25 @@ def test_sweep_parity(nkv, M):
     check(case, g)
 
 
-@pytest.mark.parametrize("nkv", [1, 2])
 @pytest.mark.parametrize("M", [6, 7, 9, 10, 11, 13, 14, 15])
+@pytest.mark.parametrize("nkv", [1, 2])
 def test_balanced_rows_other_token_counts(nkv, M):
     """The row counts the sweep skips, with 1 and 2 KV heads: balanced rows
     per XCD, whose v and gate readers take runs of columns that end inside a
     head; odd M leaves half a reader wave idle; 2 KV heads switch from 4 to
     8 K splits (and x ahead of the weights) between 11 and 12 rows."""
+    w = wl.sweep(M, nkv)
+    case = Case(w, W=_sweep_weights(nkv))
+    g = run_gpu(case)
+    check(case, g)
+
+
+@pytest.mark.parametrize("M", [6, 11, 13, 15])
+@pytest.mark.parametrize("nkv", [4, 8])
+def test_whole_heads_other_token_counts(nkv, M):
+    """The row counts the sweep skips, with 4 and 8 KV heads (whole heads
+    per XCD, 16-row tiles): odd M leaves half a reader wave idle, and x
+    moves ahead of the weights between 11 and 12 rows."""
     w = wl.sweep(M, nkv)
     case = Case(w, W=_sweep_weights(nkv))
     g = run_gpu(case)
