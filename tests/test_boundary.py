@@ -262,3 +262,24 @@ def test_run_static_refusals_before_the_device(L):
     import torch
     if not torch.cuda.is_available():
         assert L.qkvf_run_static(1152, 1, *args, 1, None) == 1
+
+
+def test_header_is_c_and_a_c_program_links_the_library(L, tmp_path):
+    """include/qkvf.h compiles as C11 with gcc, and a C program linked
+    against libqkvfront.so gets the documented launch shapes and refusals
+    (tests/c_consumer/consumer.c; no GPU call)."""
+    import subprocess
+    exe = tmp_path / "consumer"
+    src = os.path.join(ROOT, "tests", "c_consumer", "consumer.c")
+    build = subprocess.run(
+        ["gcc", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+         "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src,
+         "-L", os.path.dirname(qf.LIB_PATH), "-lqkvfront",
+         "-Wl,-rpath," + os.path.dirname(qf.LIB_PATH), "-o", str(exe)],
+        capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-3000:]
+    # Diagnostics from HIP's own headers are not ours; none may name these files.
+    for name in ("qkvf.h", "consumer.c"):
+        assert name + ":" not in build.stderr, build.stderr[-3000:]
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "failures 0" in run.stdout, run.stdout + run.stderr
